@@ -1,0 +1,181 @@
+"""Benchmark of the FP8 varlen ViT-attention path on one MI355X.
+
+One step = one forward of the whole path on one batch of synthetic input:
+dynamic quantize (amax -> ring/scale finalize -> E4M3 quantize of Q, K, V)
+followed by the varlen FP8 attention.  Default workload: 1 sequence of 8192
+tokens, 16 heads, head_dim 128 (the kernel-benchmark shape).  Inputs are
+already resident in HBM when the timed region starts; the step rotates over
+several input sets whose total exceeds the 256 MB Infinity Cache, so each
+step's bf16 reads come from HBM.
+
+Prints ONE JSON line.  Work convention: 4 * sum(n_b^2) * H * 128 flop
+(two matmuls, 2 flop per multiply-add; softmax and the lo-term MFMAs not
+counted).  Peaks: dense FP8 MFMA 5000 TFLOP/s, HBM 8000 GB/s.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FP8_PEAK_TFLOPS = 5000.0
+HBM_PEAK_GBS = 8000.0
+METRIC = "FP8 varlen ViT attn TFLOP/s incl. QKV quant (seq 8192, d=128), % fp8 peak"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", type=int, default=3)
+    p.add_argument("--sets", type=int, default=4, help="input sets rotated through (defeats the 256 MB cache)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=256, help="query rows of the oracle's attention sample")
+    return p.parse_args()
+
+
+def cpu_baseline(w, xs_host, descale_inv, rows):
+    """Time the oracle (as it stands) on a bounded sample and extrapolate to the workload."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = None
+    cores = len(os.sched_getaffinity(0))
+    q, k, v = xs_host
+    inv = descale_inv[1]
+    # quantize sample: 1/16 of Q (amax + encode), extrapolated to Q, K and V
+    n_total = 3 * q.size
+    sample = q.reshape(-1)[: q.size // 16]
+    t0 = time.perf_counter()
+    oracle.amax(sample)
+    oracle.quantize(sample, inv[0])
+    t_q = (time.perf_counter() - t0) * n_total / sample.size
+    # attention sample: `rows` query rows of sequence 0 (all heads), oracle's own codes
+    T = w.seqlens[0]
+    q8 = oracle.quantize(q[:T], inv[0])
+    k8 = oracle.quantize(k[:T], inv[1])
+    v8 = oracle.quantize(v[:T], inv[2])
+    r = np.linspace(0, T - 1, rows).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.attention_rows(q8, k8, v8, descale_inv[0], [0, T], r)
+    t_a_rows = time.perf_counter() - t0
+    t_a = t_a_rows * sum(n * n for n in w.seqlens) / (rows * T)
+    value = w.attn_flop / (t_q + t_a) / 1e12
+    return {
+        "value": value,
+        "unit": "TFLOP/s",
+        "cores": blas_threads or cores,
+        "cores_available": cores,
+        "kind": "oracle",
+        "sample": f"amax+encode of {sample.size} elements (1/16 of Q) and float64 attention of {rows} query rows x "
+                  f"{w.num_heads} heads x {T} keys; extrapolated to the full workload "
+                  f"(quantize {t_q:.2f} s + attention {t_a:.1f} s per step)",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import quantized_flash_attn_amd as qfa
+    from workloads import WORKLOADS, cu_seqlens_tensor, make_qkv
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    H, T = w.num_heads, w.total_tokens
+    n_elem = T * H * 128
+    sets = [make_qkv(w, i, device=dev) for i in range(args.sets)]
+    q8 = torch.empty((T, H, 128), dtype=torch.uint8, device=dev)
+    k8, v8 = torch.empty_like(q8), torch.empty_like(q8)
+    out = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
+    cu = cu_seqlens_tensor(w.seqlens, dev)
+    st = qfa.init_scale_state(dev)
+    scales = qfa.descale(st)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        q, k, v = sets[i % len(sets)]
+        qfa.quantize_qkv(st, "dynamic", q, k, v, q8, k8, v8)
+        qfa.fp8_varlen_attn(q8, k8, v8, scales, cu, H, out=out)
+
+    def timed(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n  # ms
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms_step_ev = timed(step, args.steps)
+    wall = time.perf_counter() - t0
+    ms_step = ms_step_ev
+
+    # component timings on the same stream
+    ms_attn = timed(lambda i: qfa.fp8_varlen_attn(q8, k8, v8, scales, cu, H, out=out), args.steps)
+    ms_quant = timed(lambda i: qfa.quantize_qkv(st, "dynamic", *sets[i % len(sets)], q8, k8, v8), args.steps)
+
+    flop = w.attn_flop
+    value = flop / (ms_step * 1e-3) / 1e12
+    attn_tflops = flop / (ms_attn * 1e-3) / 1e12
+    quant_bytes = 5 * 3 * n_elem            # amax reads 2 B, quantize reads 2 B and writes 1 B per element
+    quant_gbs = quant_bytes / (ms_quant * 1e-3) / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)",
+        "data": "synthetic (seeded bf16 Q/K/V, per-head sigma~U(0.5,3), 0.1% x20 outliers)",
+        "config": {"workload": w.name, "seqlens": list(w.seqlens), "num_heads": H, "head_dim": 128,
+                   "scaling_mode": "dynamic", "history_len": 16, "input_sets": len(sets)},
+        "frac_fp8_peak_incl_quant": round(value / FP8_PEAK_TFLOPS, 4),
+        "attention": {"ms": round(ms_attn, 4), "tflops": round(attn_tflops, 1),
+                      "frac_fp8_peak": round(attn_tflops / FP8_PEAK_TFLOPS, 4)},
+        "quantize_dynamic": {"ms": round(ms_quant, 4), "algorithmic_bytes": quant_bytes, "gbs": round(quant_gbs, 1),
+                             "frac_hbm_peak": round(quant_gbs / HBM_PEAK_GBS, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / FP8_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "attn_fwd_kernel", "flop_per_launch": flop},
+        "wall_s_timed_region": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        q, k, v = (t.cpu().float().numpy() for t in sets[0])
+        ost = oracle.ScaleState()
+        descale, inv = ost.forward_dynamic([oracle.amax(q), oracle.amax(k), oracle.amax(v)])
+        res["cpu_baseline"] = cpu_baseline(w, (q, k, v), (descale, inv), args.cpu_rows)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,171 @@
+/*
+ * qfa.h -- C ABI of the MI355X (gfx950) FP8 varlen ViT-attention library.
+ *
+ * The library implements one path: per-tensor amax of bf16 Q, K, V feeding a
+ * 16-entry circular buffer of observed amax values per tensor (dynamic
+ * scaling) or loaded amax values times a margin (static scaling); saturating
+ * bf16 -> OCP E4M3 quantization of Q, K, V; and non-causal flash attention
+ * over packed variable-length sequences on the E4M3 codes with bf16 output.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [P2] "FP8 ViT Encoder Attention" (vLLM documentation)
+ *   [P4] "FP8 vision encoder attention" (Sonar documentation)
+ *
+ * Conventions for every entry point:
+ *   - Tensors are contiguous, token-major [total_tokens, num_heads, head_dim];
+ *     head_dim must be 128.  Q, K and V share num_heads and cu_seqlens.
+ *   - Device pointers must be 16-byte aligned.  The caller owns all device
+ *     memory; the library never allocates device memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Kernels are enqueued on it; hot-path entry points never synchronise.
+ *   - Every argument is validated on the host before any HIP call, so a
+ *     non-OK status means nothing was enqueued.  A HIP launch error, or an
+ *     asynchronous error left by earlier work, is returned as QFA_ERR_HIP.
+ *     qfa_last_error() gives a thread-local message for the last failure.
+ *   - Device data is trusted: cu_seqlens contents must satisfy the rules of
+ *     qfa_fp8_varlen_attn (check with qfa_check_cu_seqlens when unsure).
+ */
+#ifndef QFA_H
+#define QFA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qfa_status {
+    QFA_OK = 0,
+    QFA_ERR_NULL = 1,        /* a required pointer is NULL */
+    QFA_ERR_SHAPE = 2,       /* negative/zero/overflowing sizes, bad num_seqs */
+    QFA_ERR_UNSUPPORTED = 3, /* head_dim != 128 */
+    QFA_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned */
+    QFA_ERR_MODE = 5,        /* mode is neither QFA_DYNAMIC nor QFA_STATIC */
+    QFA_ERR_NO_STATIC = 6,   /* QFA_STATIC on a state initialised without static amax */
+    QFA_ERR_VALUE = 7,       /* history_len not in 1..16; static amax, margin or their product not finite and > 0 */
+    QFA_ERR_STATE = 8,       /* the handle was not initialised by qfa_init_scale_state */
+    QFA_ERR_HIP = 9,         /* a HIP runtime error */
+    QFA_ERR_DATA = 10        /* qfa_check_cu_seqlens found invalid cu_seqlens contents */
+} qfa_status;
+
+typedef enum qfa_mode {
+    QFA_DYNAMIC = 0, /* observe amax, push it into the ring, scale from the ring maximum */
+    QFA_STATIC = 1   /* scale from the loaded amax times margin; no amax pass */
+} qfa_mode;
+
+#define QFA_HEAD_DIM 128
+#define QFA_MAX_HISTORY 16
+
+/*
+ * Host handle of one attention layer's scale state.  Filled by
+ * qfa_init_scale_state; the caller keeps it (by value or pointer) next to
+ * the device buffer it names.  Fields are read-only for the caller.
+ */
+typedef struct qfa_scale_state {
+    uint32_t magic;          /* QFA_STATE_MAGIC once initialised */
+    int32_t history_len;     /* ring length, 1..16 ([P2] Usage uses 16) */
+    int32_t has_static;      /* 1 if static amax values were given */
+    float static_amax[3];    /* loaded amax of Q, K, V (amax domain) */
+    float margin;            /* static multiplier ([P2] Calibrate-Once: default 1.5) */
+    void* device;            /* caller-owned device buffer, qfa_scale_state_bytes() bytes */
+} qfa_scale_state;
+
+#define QFA_STATE_MAGIC 0x31414651u /* "QFA1" */
+
+/*
+ * Host copy of the device-resident scale state (qfa_read_scale_state).
+ * Tensor index t: 0 = Q, 1 = K, 2 = V.
+ */
+typedef struct qfa_scale_snapshot {
+    float ring[3][QFA_MAX_HISTORY]; /* observed amax values; unused slots are 0 */
+    float amax_observed[3];         /* amax seen by the last dynamic forward */
+    float amax_eff[3];              /* effective amax of the last forward */
+    float descale[3];               /* s_t = fp32(max(amax_eff, 2^-100) / 448) */
+    float inv[3];                   /* fp32(448 / max(amax_eff, 2^-100)) */
+    int32_t cursor;                 /* dynamic forwards so far */
+    int32_t history_len;
+} qfa_scale_snapshot;
+
+/* Bytes of device memory a scale state needs (a few KiB). */
+size_t qfa_scale_state_bytes(void);
+
+/*
+ * Initialise a scale state ([P2] Usage: dynamic scaling from a 16-entry
+ * circular buffer of observed amax values; [P2] Calibrate-Once, Reuse
+ * Workflow and [P4] Create static scales: loaded scales times a save margin,
+ * default 1.5).
+ *   st           host handle to fill (out)
+ *   device_buf   device buffer of qfa_scale_state_bytes() bytes, 16-B aligned
+ *   history_len  ring length, 1..16 (16 for the pages' behaviour)
+ *   static_amax  host float[3] amax values of Q, K, V for static mode, or NULL
+ *                (then QFA_STATIC is refused with QFA_ERR_NO_STATIC)
+ *   margin       static multiplier, finite and > 0 (1.5 is the pages' default;
+ *                pass 1.0 for values that already include the margin);
+ *                ignored when static_amax is NULL
+ * Enqueues one small kernel that zeroes the ring and cursor and stores the
+ * static effective amax fp32(static_amax * margin).  Re-initialising a state
+ * resets it.
+ */
+qfa_status qfa_init_scale_state(qfa_scale_state* st, void* device_buf, int history_len,
+                                const float* static_amax, float margin, void* stream);
+
+/*
+ * One forward of the quantizer ([P2] intro: Q/K/V quantized on the fly to FP8
+ * before the attention call).
+ *   QFA_DYNAMIC: amax_t = max|x| over tensor t; ring[t][cursor % history_len]
+ *     = amax_t; cursor += 1; amax_eff[t] = max(ring[t][:]).
+ *   QFA_STATIC:  amax_eff[t] = fp32(static_amax[t] * margin); ring untouched.
+ *   Both: a = max(amax_eff, 2^-100); descale = fp32(a / 448); inv =
+ *     fp32(448 / a); code = E4M3(fp32(x * inv[t])) rounded to nearest even,
+ *     saturated to +-448, sign of zero kept.
+ *   q, k, v      device bf16 [total_tokens, num_heads, head_dim]
+ *   q8, k8, v8   device uint8 E4M3 codes, same shape (out)
+ * total_tokens may be 0 (the forward still records amax 0 in dynamic mode).
+ * Forwards on one state must be ordered on one stream (single-writer ring);
+ * distinct states are independent.
+ */
+qfa_status qfa_quantize_qkv(const qfa_scale_state* st, int mode, const void* q, const void* k,
+                            const void* v, int64_t total_tokens, int num_heads, int head_dim,
+                            uint8_t* q8, uint8_t* k8, uint8_t* v8, void* stream);
+
+/* Device pointer to float[3] {s_q, s_k, s_v} inside the state (valid after a forward). */
+const float* qfa_descale_ptr(const qfa_scale_state* st);
+
+/*
+ * Varlen FP8 attention with per-tensor scales ([P4] Requirements: a
+ * per-tensor FP8 varlen attention over packed variable-length image batches).
+ *   out[i,h,:] = sum_j softmax_j(s_q*s_k*<q_i,k_j>/sqrt(128)) * s_v * v_j
+ * over the keys j of the sequence that contains token i, non-causal.
+ *   q8, k8, v8     device E4M3 codes [total_tokens, num_heads, 128]
+ *   scales         device float[3] {s_q, s_k, s_v} (e.g. qfa_descale_ptr)
+ *   cu_seqlens     device int32[num_seqs + 1]: cu[0] = 0, non-decreasing,
+ *                  cu[num_seqs] = total_tokens; empty sequences are allowed
+ *   out            device bf16 [total_tokens, num_heads, 128] (out)
+ * total_tokens must be below 2^31.  The kernel uses E4M3 probabilities split
+ * into two terms (hi + lo) for the P*V product and float32 accumulation.
+ */
+qfa_status qfa_fp8_varlen_attn(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                               const float* scales, const int32_t* cu_seqlens, int num_seqs,
+                               int64_t total_tokens, int num_heads, int head_dim, void* out,
+                               void* stream);
+
+/*
+ * Debug/checkpoint helpers (synchronise `stream`; not for the hot path).
+ * qfa_read_scale_state copies the device state to *out.
+ * qfa_check_cu_seqlens reads cu_seqlens back and returns QFA_ERR_DATA unless
+ * cu[0] = 0, cu is non-decreasing and cu[num_seqs] = total_tokens.
+ */
+qfa_status qfa_read_scale_state(const qfa_scale_state* st, qfa_scale_snapshot* out, void* stream);
+qfa_status qfa_check_cu_seqlens(const int32_t* cu_seqlens, int num_seqs, int64_t total_tokens,
+                                void* stream);
+
+/* Static text for a status; thread-local detail of the last failure on this thread. */
+const char* qfa_status_string(qfa_status s);
+const char* qfa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QFA_H */

@@ -38,11 +38,17 @@ def _softmax_rows(s):
     return p / p.sum(axis=-1, keepdims=True)
 
 
-def attention(q8, k8, v8, descale, cu_seqlens) -> np.ndarray:
-    """Full output, float64 ``[T, H, D]``, from uint8 codes ``[T, H, D]``."""
+def attention(q8, k8, v8, descale, cu_seqlens, magnitude=False):
+    """Full output, float64 ``[T, H, D]``, from uint8 codes ``[T, H, D]``.
+
+    With ``magnitude=True`` also returns ``M = P |V|`` (same shape): for each
+    output element, the probability-weighted mean magnitude of the values it
+    averages.  The tests use it as the element's scale when comparing.
+    """
     T, H, D = q8.shape
     cu = _check_cu(cu_seqlens, T)
     out = np.zeros((T, H, D), dtype=np.float64)
+    mag = np.zeros((T, H, D), dtype=np.float64) if magnitude else None
     inv_sqrt_d = 1.0 / math.sqrt(D)
     for b in range(cu.size - 1):
         lo, hi = int(cu[b]), int(cu[b + 1])
@@ -54,20 +60,24 @@ def attention(q8, k8, v8, descale, cu_seqlens) -> np.ndarray:
             vf = _dequant(v8[lo:hi, h], descale[2])
             p = _softmax_rows(qf @ kf.T * inv_sqrt_d)
             out[lo:hi, h] = p @ vf
-    return out
+            if magnitude:
+                mag[lo:hi, h] = p @ np.abs(vf)
+    return (out, mag) if magnitude else out
 
 
-def attention_rows(q8, k8, v8, descale, cu_seqlens, rows) -> np.ndarray:
+def attention_rows(q8, k8, v8, descale, cu_seqlens, rows, magnitude=False) -> np.ndarray:
     """Output rows ``rows`` (global token indices) only: float64 ``[len(rows), H, D]``.
 
     Each query row attends to every key of its own sequence, as in
     ``attention``; this evaluates the same definition for a subset of rows.
+    ``magnitude`` as in ``attention``.
     """
     T, H, D = q8.shape
     cu = _check_cu(cu_seqlens, T)
     rows = np.asarray(rows, dtype=np.int64)
     seq_of = np.searchsorted(cu, rows, side="right") - 1
     out = np.zeros((rows.size, H, D), dtype=np.float64)
+    mag = np.zeros((rows.size, H, D), dtype=np.float64) if magnitude else None
     inv_sqrt_d = 1.0 / math.sqrt(D)
     for b in np.unique(seq_of):
         lo, hi = int(cu[b]), int(cu[b + 1])
@@ -78,4 +88,6 @@ def attention_rows(q8, k8, v8, descale, cu_seqlens, rows) -> np.ndarray:
             vf = _dequant(v8[lo:hi, h], descale[2])
             p = _softmax_rows(qf @ kf.T * inv_sqrt_d)
             out[sel, h] = p @ vf
-    return out
+            if magnitude:
+                mag[sel, h] = p @ np.abs(vf)
+    return (out, mag) if magnitude else out

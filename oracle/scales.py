@@ -87,6 +87,9 @@ class ScaleState:
             m = np.float32(self.margin)
             if not np.isfinite(m) or m <= 0:
                 raise ValueError("margin must be finite and positive")
+            with np.errstate(over="ignore"):
+                if not np.all(np.isfinite(static_amax_eff(sa, m))):
+                    raise ValueError("static amax times margin overflows float32")
             self.static_amax = sa
 
     def forward_dynamic(self, observed) -> tuple:

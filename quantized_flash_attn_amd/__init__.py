@@ -1,0 +1,275 @@
+"""Python binding of the MI355X FP8 varlen ViT-attention library (libqfa.so).
+
+Argument marshalling only: every step of the path runs in the HIP kernels
+behind the C ABI declared in ``include/qfa.h``.  PyTorch supplies device
+memory and the current stream.  There is no fallback: importing this package
+without the built library, or calling it on tensors that are not on a GPU,
+raises.
+
+Entry points (same names as the C ABI without the ``qfa_`` prefix):
+
+* ``scale_state_bytes()``
+* ``init_scale_state(device=..., history_len=16, static_amax=None, margin=1.5)``
+  -> ``ScaleState``
+* ``quantize_qkv(state, mode, q, k, v, q8=None, k8=None, v8=None)`` -> ``(q8, k8, v8)``
+* ``descale(state)`` -> device float32[3] view {s_q, s_k, s_v}
+* ``fp8_varlen_attn(q8, k8, v8, scales, cu_seqlens, num_heads, head_dim=128, out=None)``
+* ``read_scale_state(state)`` -> dict (synchronises; for tests and checkpoints)
+* ``check_cu_seqlens(cu_seqlens, total_tokens)`` (synchronises)
+"""
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqfa.so")
+
+DYNAMIC = 0
+STATIC = 1
+HEAD_DIM = 128
+MAX_HISTORY = 16
+
+_MODES = {"dynamic": DYNAMIC, "static": STATIC, DYNAMIC: DYNAMIC, STATIC: STATIC}
+
+STATUS = {
+    0: "QFA_OK",
+    1: "QFA_ERR_NULL",
+    2: "QFA_ERR_SHAPE",
+    3: "QFA_ERR_UNSUPPORTED",
+    4: "QFA_ERR_ALIGN",
+    5: "QFA_ERR_MODE",
+    6: "QFA_ERR_NO_STATIC",
+    7: "QFA_ERR_VALUE",
+    8: "QFA_ERR_STATE",
+    9: "QFA_ERR_HIP",
+    10: "QFA_ERR_DATA",
+}
+
+
+class QfaError(RuntimeError):
+    """A non-OK status from the C ABI."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class _State(ctypes.Structure):
+    _fields_ = [
+        ("magic", ctypes.c_uint32),
+        ("history_len", ctypes.c_int32),
+        ("has_static", ctypes.c_int32),
+        ("static_amax", ctypes.c_float * 3),
+        ("margin", ctypes.c_float),
+        ("device", ctypes.c_void_p),
+    ]
+
+
+class _Snapshot(ctypes.Structure):
+    _fields_ = [
+        ("ring", (ctypes.c_float * MAX_HISTORY) * 3),
+        ("amax_observed", ctypes.c_float * 3),
+        ("amax_eff", ctypes.c_float * 3),
+        ("descale", ctypes.c_float * 3),
+        ("inv", ctypes.c_float * 3),
+        ("cursor", ctypes.c_int32),
+        ("history_len", ctypes.c_int32),
+    ]
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is missing: build it with `python -m quantized_flash_attn_amd.build` "
+            "(there is no non-HIP fallback)"
+        )
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+    sigs = {
+        "qfa_scale_state_bytes": (ctypes.c_size_t, []),
+        "qfa_init_scale_state": (i32, [ctypes.POINTER(_State), vp, i32, ctypes.POINTER(ctypes.c_float), f32, vp]),
+        "qfa_quantize_qkv": (i32, [ctypes.POINTER(_State), i32, vp, vp, vp, i64, i32, i32, vp, vp, vp, vp]),
+        "qfa_descale_ptr": (vp, [ctypes.POINTER(_State)]),
+        "qfa_fp8_varlen_attn": (i32, [vp, vp, vp, vp, vp, i32, i64, i32, i32, vp, vp]),
+        "qfa_read_scale_state": (i32, [ctypes.POINTER(_State), ctypes.POINTER(_Snapshot), vp]),
+        "qfa_check_cu_seqlens": (i32, [vp, i32, i64, vp]),
+        "qfa_status_string": (ctypes.c_char_p, [i32]),
+        "qfa_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+#: C symbols the header declares (checked by the tests against the library's exports).
+EXPORTS = (
+    "qfa_scale_state_bytes",
+    "qfa_init_scale_state",
+    "qfa_quantize_qkv",
+    "qfa_descale_ptr",
+    "qfa_fp8_varlen_attn",
+    "qfa_read_scale_state",
+    "qfa_check_cu_seqlens",
+    "qfa_status_string",
+    "qfa_last_error",
+)
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def raw_library():
+    """The loaded ctypes library (for ABI-level tests)."""
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise QfaError(status, _lib.qfa_last_error().decode())
+
+
+def _stream_ptr(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _require_gpu(*tensors):
+    for t in tensors:
+        if not t.is_cuda:
+            raise ValueError("tensors must live on a GPU (no CPU fallback)")
+
+
+def scale_state_bytes() -> int:
+    return int(_lib.qfa_scale_state_bytes())
+
+
+class ScaleState:
+    """One layer's scale state: host handle plus caller-owned device buffer."""
+
+    def __init__(self, handle: _State, buffer: torch.Tensor):
+        self._handle = handle
+        self.buffer = buffer
+
+    @property
+    def handle(self):
+        return ctypes.byref(self._handle)
+
+    @property
+    def history_len(self) -> int:
+        return int(self._handle.history_len)
+
+    @property
+    def has_static(self) -> bool:
+        return bool(self._handle.has_static)
+
+
+def init_scale_state(device=None, history_len: int = MAX_HISTORY, static_amax=None, margin: float = 1.5,
+                     buffer: torch.Tensor = None) -> ScaleState:
+    """Allocate (or reuse ``buffer``) and initialise a scale state on ``device``."""
+    if buffer is None:
+        device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+        buffer = torch.zeros(scale_state_bytes(), dtype=torch.uint8, device=device)
+    _require_gpu(buffer)
+    handle = _State()
+    sa = None
+    if static_amax is not None:
+        vals = [float(x) for x in static_amax]
+        if len(vals) != 3:
+            raise ValueError("static_amax needs three values (q, k, v)")
+        sa = (ctypes.c_float * 3)(*vals)
+    with torch.cuda.device(buffer.device):
+        _check(_lib.qfa_init_scale_state(ctypes.byref(handle), ctypes.c_void_p(buffer.data_ptr()), int(history_len),
+                                         sa, ctypes.c_float(margin), _stream_ptr(buffer.device)))
+    return ScaleState(handle, buffer)
+
+
+def _qkv_shape(q):
+    if q.dim() != 3:
+        raise ValueError("tensors must be [tokens, heads, head_dim]")
+    return q.shape[0], q.shape[1], q.shape[2]
+
+
+def quantize_qkv(state: ScaleState, mode, q, k, v, q8=None, k8=None, v8=None):
+    """One forward: amax/ring (dynamic) or static scales, then E4M3 codes of q, k, v."""
+    _require_gpu(q, k, v)
+    if mode not in _MODES:
+        raise ValueError("mode must be 'dynamic' or 'static'")
+    T, H, D = _qkv_shape(q)
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16 or tuple(t.shape) != (T, H, D) or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous bf16 tensors of one shape")
+    outs = []
+    for o in (q8, k8, v8):
+        if o is None:
+            o = torch.empty((T, H, D), dtype=torch.uint8, device=q.device)
+        elif o.dtype != torch.uint8 or tuple(o.shape) != (T, H, D) or not o.is_contiguous():
+            raise ValueError("q8, k8, v8 must be contiguous uint8 tensors of the input shape")
+        outs.append(o)
+    with torch.cuda.device(q.device):
+        _check(_lib.qfa_quantize_qkv(state.handle, _MODES[mode], q.data_ptr(), k.data_ptr(), v.data_ptr(), T, H, D,
+                                     outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(),
+                                     _stream_ptr(q.device)))
+    return tuple(outs)
+
+
+def descale(state: ScaleState) -> torch.Tensor:
+    """Device float32[3] {s_q, s_k, s_v}: a view into the state buffer."""
+    ptr = _lib.qfa_descale_ptr(state.handle)
+    if not ptr:
+        raise QfaError(8, "state not initialised")
+    off = ptr - state.buffer.data_ptr()
+    return state.buffer[off:off + 12].view(torch.float32)
+
+
+def fp8_varlen_attn(q8, k8, v8, scales, cu_seqlens, num_heads=None, head_dim=HEAD_DIM, out=None):
+    """bf16 attention output ``[T, H, 128]`` from E4M3 codes and per-tensor scales."""
+    _require_gpu(q8, k8, v8, scales, cu_seqlens)
+    T, H, D = _qkv_shape(q8)
+    if num_heads is not None and num_heads != H:
+        raise ValueError("num_heads does not match q8")
+    for t in (q8, k8, v8):
+        if t.dtype != torch.uint8 or tuple(t.shape) != (T, H, D) or not t.is_contiguous():
+            raise ValueError("q8, k8, v8 must be contiguous uint8 tensors of one shape")
+    if scales.dtype != torch.float32 or scales.numel() < 3:
+        raise ValueError("scales must be float32[3]")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be int32[num_seqs + 1]")
+    if out is None:
+        out = torch.empty((T, H, D), dtype=torch.bfloat16, device=q8.device)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (T, H, D) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 tensor of the input shape")
+    with torch.cuda.device(q8.device):
+        _check(_lib.qfa_fp8_varlen_attn(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), scales.data_ptr(),
+                                        cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, T, H, head_dim,
+                                        out.data_ptr(), _stream_ptr(q8.device)))
+    return out
+
+
+def read_scale_state(state: ScaleState) -> dict:
+    """Synchronous copy of the device state (ring, cursor, amax, descale, inv)."""
+    snap = _Snapshot()
+    with torch.cuda.device(state.buffer.device):
+        _check(_lib.qfa_read_scale_state(state.handle, ctypes.byref(snap), _stream_ptr(state.buffer.device)))
+    hist = int(snap.history_len)
+    return {
+        "ring": [[float(snap.ring[t][j]) for j in range(hist)] for t in range(3)],
+        "amax_observed": [float(x) for x in snap.amax_observed],
+        "amax_eff": [float(x) for x in snap.amax_eff],
+        "descale": [float(x) for x in snap.descale],
+        "inv": [float(x) for x in snap.inv],
+        "cursor": int(snap.cursor),
+        "history_len": hist,
+    }
+
+
+def check_cu_seqlens(cu_seqlens, total_tokens: int):
+    """Validate device cu_seqlens contents (synchronises); raises QfaError(QFA_ERR_DATA)."""
+    _require_gpu(cu_seqlens)
+    with torch.cuda.device(cu_seqlens.device):
+        _check(_lib.qfa_check_cu_seqlens(cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, int(total_tokens),
+                                         _stream_ptr(cu_seqlens.device)))

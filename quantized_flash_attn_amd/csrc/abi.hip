@@ -1,0 +1,212 @@
+// C ABI of the library: argument validation (before any HIP call), status
+// codes, thread-local error text, and dispatch to the kernel launchers.
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "qfa_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+qfa_status fail(qfa_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+qfa_status ok() {
+    g_last_error[0] = '\0';
+    return QFA_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Surface an asynchronous error left by earlier work on this thread's device
+// before enqueuing more.
+qfa_status check_pending(const char* where) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(QFA_ERR_HIP, "%s: pending HIP error: %s", where, hipGetErrorString(e));
+    return QFA_OK;
+}
+
+qfa_status check_launch(hipError_t e, const char* where) {
+    if (e != hipSuccess) return fail(QFA_ERR_HIP, "%s: HIP error: %s", where, hipGetErrorString(e));
+    return ok();
+}
+
+// Shared checks of a [T, H, D] tensor triple.  Returns elements per tensor.
+qfa_status check_shape(int64_t total_tokens, int num_heads, int head_dim, int64_t* elems, const char* where) {
+    if (head_dim != QFA_HEAD_DIM) return fail(QFA_ERR_UNSUPPORTED, "%s: head_dim %d (only 128 is supported)", where, head_dim);
+    if (num_heads <= 0) return fail(QFA_ERR_SHAPE, "%s: num_heads %d must be positive", where, num_heads);
+    if (total_tokens < 0) return fail(QFA_ERR_SHAPE, "%s: total_tokens %lld is negative", where, (long long)total_tokens);
+    // elements per tensor must fit comfortably in int64 byte offsets
+    if (total_tokens > (INT64_C(1) << 40) / ((int64_t)num_heads * head_dim))
+        return fail(QFA_ERR_SHAPE, "%s: tensor too large", where);
+    *elems = total_tokens * num_heads * head_dim;
+    return QFA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t qfa_scale_state_bytes(void) { return sizeof(qfa::DeviceState); }
+
+const char* qfa_status_string(qfa_status s) {
+    switch (s) {
+        case QFA_OK: return "ok";
+        case QFA_ERR_NULL: return "null pointer";
+        case QFA_ERR_SHAPE: return "invalid shape";
+        case QFA_ERR_UNSUPPORTED: return "unsupported head_dim (only 128)";
+        case QFA_ERR_ALIGN: return "device pointer not 16-byte aligned";
+        case QFA_ERR_MODE: return "invalid mode";
+        case QFA_ERR_NO_STATIC: return "static mode without static amax";
+        case QFA_ERR_VALUE: return "invalid value";
+        case QFA_ERR_STATE: return "scale state not initialised";
+        case QFA_ERR_HIP: return "HIP runtime error";
+        case QFA_ERR_DATA: return "invalid cu_seqlens contents";
+    }
+    return "unknown status";
+}
+
+const char* qfa_last_error(void) { return g_last_error; }
+
+qfa_status qfa_init_scale_state(qfa_scale_state* st, void* device_buf, int history_len, const float* static_amax,
+                                float margin, void* stream) {
+    const char* where = "qfa_init_scale_state";
+    if (!st || !device_buf) return fail(QFA_ERR_NULL, "%s: null handle or device buffer", where);
+    if (!aligned16(device_buf)) return fail(QFA_ERR_ALIGN, "%s: device buffer not 16-byte aligned", where);
+    if (history_len < 1 || history_len > QFA_MAX_HISTORY)
+        return fail(QFA_ERR_VALUE, "%s: history_len %d not in 1..16", where, history_len);
+    float eff[3] = {0.0f, 0.0f, 0.0f};
+    if (static_amax) {
+        if (!std::isfinite(margin) || !(margin > 0.0f))
+            return fail(QFA_ERR_VALUE, "%s: margin must be finite and positive", where);
+        for (int t = 0; t < 3; ++t) {
+            if (!std::isfinite(static_amax[t]) || !(static_amax[t] > 0.0f))
+                return fail(QFA_ERR_VALUE, "%s: static amax[%d] must be finite and positive", where, t);
+            volatile float prod = static_amax[t] * margin;  // one float32 multiply, as on the device
+            eff[t] = prod;
+            if (!std::isfinite(eff[t]))
+                return fail(QFA_ERR_VALUE, "%s: static amax[%d] * margin overflows float32", where, t);
+        }
+    }
+    qfa_status ps = check_pending(where);
+    if (ps != QFA_OK) return ps;
+    const hipError_t e = qfa::launch_init_state((qfa::DeviceState*)device_buf, history_len, eff, (hipStream_t)stream);
+    if (e != hipSuccess) return check_launch(e, where);
+    st->magic = QFA_STATE_MAGIC;
+    st->history_len = history_len;
+    st->has_static = static_amax ? 1 : 0;
+    for (int t = 0; t < 3; ++t) st->static_amax[t] = static_amax ? static_amax[t] : 0.0f;
+    st->margin = static_amax ? margin : 1.0f;
+    st->device = device_buf;
+    return ok();
+}
+
+qfa_status qfa_quantize_qkv(const qfa_scale_state* st, int mode, const void* q, const void* k, const void* v,
+                            int64_t total_tokens, int num_heads, int head_dim, uint8_t* q8, uint8_t* k8,
+                            uint8_t* v8, void* stream) {
+    const char* where = "qfa_quantize_qkv";
+    if (!st) return fail(QFA_ERR_NULL, "%s: null state handle", where);
+    if (st->magic != QFA_STATE_MAGIC || !st->device) return fail(QFA_ERR_STATE, "%s: state not initialised", where);
+    if (mode != QFA_DYNAMIC && mode != QFA_STATIC) return fail(QFA_ERR_MODE, "%s: mode %d", where, mode);
+    if (mode == QFA_STATIC && !st->has_static)
+        return fail(QFA_ERR_NO_STATIC, "%s: state was initialised without static amax", where);
+    int64_t n = 0;
+    qfa_status s = check_shape(total_tokens, num_heads, head_dim, &n, where);
+    if (s != QFA_OK) return s;
+    if (n > 0 && (!q || !k || !v || !q8 || !k8 || !v8)) return fail(QFA_ERR_NULL, "%s: null tensor pointer", where);
+    if (n > 0 && !(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(q8) && aligned16(k8) && aligned16(v8)))
+        return fail(QFA_ERR_ALIGN, "%s: tensor pointer not 16-byte aligned", where);
+    s = check_pending(where);
+    if (s != QFA_OK) return s;
+    qfa::DeviceState* ds = (qfa::DeviceState*)st->device;
+    const hipError_t e =
+        mode == QFA_DYNAMIC
+            ? qfa::launch_quantize_dynamic(ds, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, n, q8, k8,
+                                           v8, (hipStream_t)stream)
+            : qfa::launch_quantize_static(ds, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, n, q8, k8,
+                                          v8, (hipStream_t)stream);
+    return check_launch(e, where);
+}
+
+const float* qfa_descale_ptr(const qfa_scale_state* st) {
+    if (!st || st->magic != QFA_STATE_MAGIC || !st->device) return nullptr;
+    return ((const qfa::DeviceState*)st->device)->descale;
+}
+
+qfa_status qfa_fp8_varlen_attn(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* scales,
+                               const int32_t* cu_seqlens, int num_seqs, int64_t total_tokens, int num_heads,
+                               int head_dim, void* out, void* stream) {
+    const char* where = "qfa_fp8_varlen_attn";
+    int64_t n = 0;
+    qfa_status s = check_shape(total_tokens, num_heads, head_dim, &n, where);
+    if (s != QFA_OK) return s;
+    if (num_seqs < 1) return fail(QFA_ERR_SHAPE, "%s: num_seqs %d must be at least 1", where, num_seqs);
+    if (total_tokens >= (INT64_C(1) << 31)) return fail(QFA_ERR_SHAPE, "%s: total_tokens must be below 2^31", where);
+    if (!scales || !cu_seqlens) return fail(QFA_ERR_NULL, "%s: null scales or cu_seqlens", where);
+    if (n > 0 && (!q8 || !k8 || !v8 || !out)) return fail(QFA_ERR_NULL, "%s: null tensor pointer", where);
+    if (n > 0 && !(aligned16(q8) && aligned16(k8) && aligned16(v8) && aligned16(out)))
+        return fail(QFA_ERR_ALIGN, "%s: tensor pointer not 16-byte aligned", where);
+    if (((uintptr_t)scales & 3u) || ((uintptr_t)cu_seqlens & 3u))
+        return fail(QFA_ERR_ALIGN, "%s: scales / cu_seqlens not 4-byte aligned", where);
+    s = check_pending(where);
+    if (s != QFA_OK) return s;
+    if (n == 0) return ok();
+    const hipError_t e = qfa::launch_attention(q8, k8, v8, scales, cu_seqlens, num_seqs, (int)total_tokens, num_heads,
+                                               out, (hipStream_t)stream);
+    return check_launch(e, where);
+}
+
+qfa_status qfa_read_scale_state(const qfa_scale_state* st, qfa_scale_snapshot* out, void* stream) {
+    const char* where = "qfa_read_scale_state";
+    if (!st || !out) return fail(QFA_ERR_NULL, "%s: null pointer", where);
+    if (st->magic != QFA_STATE_MAGIC || !st->device) return fail(QFA_ERR_STATE, "%s: state not initialised", where);
+    qfa::DeviceState h;
+    hipError_t e = hipMemcpyAsync(&h, st->device, offsetof(qfa::DeviceState, partial), hipMemcpyDeviceToHost,
+                                  (hipStream_t)stream);
+    if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return check_launch(e, where);
+    memcpy(out->ring, h.ring, sizeof(out->ring));
+    memcpy(out->amax_observed, h.amax_observed, sizeof(out->amax_observed));
+    memcpy(out->amax_eff, h.amax_eff, sizeof(out->amax_eff));
+    memcpy(out->descale, h.descale, sizeof(out->descale));
+    memcpy(out->inv, h.inv, sizeof(out->inv));
+    out->cursor = h.cursor;
+    out->history_len = h.history_len;
+    return ok();
+}
+
+qfa_status qfa_check_cu_seqlens(const int32_t* cu_seqlens, int num_seqs, int64_t total_tokens, void* stream) {
+    const char* where = "qfa_check_cu_seqlens";
+    if (!cu_seqlens) return fail(QFA_ERR_NULL, "%s: null cu_seqlens", where);
+    if (num_seqs < 1) return fail(QFA_ERR_SHAPE, "%s: num_seqs %d must be at least 1", where, num_seqs);
+    if (total_tokens < 0 || total_tokens >= (INT64_C(1) << 31)) return fail(QFA_ERR_SHAPE, "%s: total_tokens out of range", where);
+    int32_t* h = (int32_t*)malloc(sizeof(int32_t) * ((size_t)num_seqs + 1));
+    if (!h) return fail(QFA_ERR_SHAPE, "%s: host allocation failed", where);
+    hipError_t e = hipMemcpyAsync(h, cu_seqlens, sizeof(int32_t) * ((size_t)num_seqs + 1), hipMemcpyDeviceToHost,
+                                  (hipStream_t)stream);
+    if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) {
+        free(h);
+        return check_launch(e, where);
+    }
+    qfa_status s = QFA_OK;
+    if (h[0] != 0) s = fail(QFA_ERR_DATA, "%s: cu_seqlens[0] = %d, expected 0", where, h[0]);
+    for (int b = 0; s == QFA_OK && b < num_seqs; ++b)
+        if (h[b + 1] < h[b]) s = fail(QFA_ERR_DATA, "%s: cu_seqlens decreases at %d", where, b);
+    if (s == QFA_OK && h[num_seqs] != total_tokens)
+        s = fail(QFA_ERR_DATA, "%s: cu_seqlens[%d] = %d, expected %lld", where, num_seqs, h[num_seqs],
+                 (long long)total_tokens);
+    free(h);
+    return s == QFA_OK ? ok() : s;
+}
+
+}  // extern "C"

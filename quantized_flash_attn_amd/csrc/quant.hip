@@ -1,0 +1,236 @@
+// Scale state, per-tensor amax and bf16 -> E4M3 quantization for gfx950.
+//
+// Dynamic scaling ("FP8 ViT Encoder Attention", Usage; "FP8 vision encoder
+// attention", Enable FP8 attention): each forward observes the amax of Q, K
+// and V, records it in a 16-entry circular buffer per tensor and derives the
+// forward's scale from the buffer's maximum.  Static scaling ("FP8 ViT
+// Encoder Attention", Calibrate-Once, Reuse Workflow): loaded amax values
+// times a margin.  Quantization ("FP8 ViT Encoder Attention", intro) turns
+// Q/K/V into FP8 before the attention call.
+//
+// Kernels (all HBM-streaming except the single-workgroup finalize):
+//   amax_partial_kernel    grid (P, 3): max of |x| as bf16 bit patterns,
+//                          one partial per workgroup, no atomics
+//   finalize_dynamic_kernel  one workgroup: reduce partials, push the ring,
+//                          cursor++, compute descale and inv (single writer)
+//   quantize_kernel        grid (G, 3): x * inv -> clamp +-448 -> E4M3 (RNE)
+
+#include "qfa_internal.h"
+
+// Every float operation here must round exactly as written (bit-exact codes).
+#pragma clang fp contract(off)
+
+namespace qfa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr float kFp8Max = 448.0f;
+constexpr float kAmaxFloor = 0x1p-100f;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// a = max(amax_eff, 2^-100); descale = fp32(a / 448); inv = fp32(448 / a).
+// Both divisions are IEEE float32 (correctly rounded; no fast-math).
+__device__ inline void scales_from_amax(float amax_eff, float* descale, float* inv) {
+    const float a = fmaxf(amax_eff, kAmaxFloor);
+    *descale = a / kFp8Max;
+    *inv = kFp8Max / a;
+}
+
+__global__ void init_state_kernel(DeviceState* st, int history_len, float e0, float e1, float e2) {
+    const int t = threadIdx.x;
+    if (t < 3 * QFA_MAX_HISTORY) (&st->ring[0][0])[t] = 0.0f;
+    if (t < 3) {
+        st->amax_observed[t] = 0.0f;
+        st->amax_eff[t] = 0.0f;
+        float d, i;
+        scales_from_amax(0.0f, &d, &i);
+        st->descale[t] = d;
+        st->inv[t] = i;
+        st->static_eff[t] = t == 0 ? e0 : (t == 1 ? e1 : e2);
+    }
+    if (t == 0) {
+        st->cursor = 0;
+        st->history_len = history_len;
+    }
+}
+
+__device__ inline uint32_t wave_max_u32(uint32_t m) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+    return m;
+}
+
+// |x| of a bf16 is its bit pattern with the sign cleared; for finite values
+// the integer order of those patterns is the order of the magnitudes, so the
+// integer maximum is exact and independent of reduction order.
+__device__ inline uint32_t max_abs_bits(u32x4 w, uint32_t m) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        m = max(m, w[j] & 0x7FFFu);
+        m = max(m, (w[j] >> 16) & 0x7FFFu);
+    }
+    return m;
+}
+
+__global__ __launch_bounds__(kThreads) void amax_partial_kernel(const u32x4* __restrict__ q, const u32x4* __restrict__ k,
+                                                                const u32x4* __restrict__ v, int64_t n_chunks,
+                                                                uint32_t* __restrict__ partial) {
+    const int t = blockIdx.y;
+    const u32x4* __restrict__ src = t == 0 ? q : (t == 1 ? k : v);
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    uint32_t m = 0;
+    for (; i + 3 * stride < n_chunks; i += 4 * stride) {
+        const u32x4 a = __builtin_nontemporal_load(src + i);
+        const u32x4 b = __builtin_nontemporal_load(src + i + stride);
+        const u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
+        const u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
+        m = max_abs_bits(a, m);
+        m = max_abs_bits(b, m);
+        m = max_abs_bits(c, m);
+        m = max_abs_bits(d, m);
+    }
+    for (; i < n_chunks; i += stride) m = max_abs_bits(__builtin_nontemporal_load(src + i), m);
+    m = wave_max_u32(m);
+    __shared__ uint32_t red[kThreads / 64];
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t r = red[0];
+#pragma unroll
+        for (int w = 1; w < kThreads / 64; ++w) r = max(r, red[w]);
+        partial[t * kMaxPartials + blockIdx.x] = r;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void finalize_dynamic_kernel(DeviceState* st, int n_partials) {
+    __shared__ uint32_t red[3][kThreads / 64];
+    for (int t = 0; t < 3; ++t) {
+        uint32_t m = 0;
+        for (int j = threadIdx.x; j < n_partials; j += kThreads) m = max(m, st->partial[t][j]);
+        m = wave_max_u32(m);
+        if ((threadIdx.x & 63) == 0) red[t][threadIdx.x >> 6] = m;
+    }
+    __syncthreads();
+    if (threadIdx.x != 0) return;
+    const int cursor = st->cursor;
+    const int hist = st->history_len;
+    const int slot = cursor % hist;
+    for (int t = 0; t < 3; ++t) {
+        uint32_t bits = red[t][0];
+        for (int w = 1; w < kThreads / 64; ++w) bits = max(bits, red[t][w]);
+        const float amax = __uint_as_float(bits << 16);
+        st->ring[t][slot] = amax;
+        st->amax_observed[t] = amax;
+        float eff = 0.0f;
+        for (int j = 0; j < hist; ++j) eff = fmaxf(eff, st->ring[t][j]);
+        st->amax_eff[t] = eff;
+        float d, i;
+        scales_from_amax(eff, &d, &i);
+        st->descale[t] = d;
+        st->inv[t] = i;
+    }
+    st->cursor = cursor + 1;
+}
+
+// 8 bf16 values -> 8 E4M3 codes: fp32 multiply (RNE), clamp to +-448 (the
+// conversion instruction alone turns values beyond the format into NaN),
+// then v_cvt_pk_fp8_f32 (OCP E4M3 on gfx950, RNE, sign of zero kept).
+__device__ inline u32x2 quantize8(u32x4 w, float inv) {
+    u32x2 out;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const uint32_t w0 = w[2 * j], w1 = w[2 * j + 1];
+        float y0 = __uint_as_float(w0 << 16) * inv;
+        float y1 = __uint_as_float(w0 & 0xFFFF0000u) * inv;
+        float y2 = __uint_as_float(w1 << 16) * inv;
+        float y3 = __uint_as_float(w1 & 0xFFFF0000u) * inv;
+        y0 = __builtin_amdgcn_fmed3f(y0, -kFp8Max, kFp8Max);
+        y1 = __builtin_amdgcn_fmed3f(y1, -kFp8Max, kFp8Max);
+        y2 = __builtin_amdgcn_fmed3f(y2, -kFp8Max, kFp8Max);
+        y3 = __builtin_amdgcn_fmed3f(y3, -kFp8Max, kFp8Max);
+        int r = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+        r = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, r, true);
+        out[j] = (uint32_t)r;
+    }
+    return out;
+}
+
+template <bool kStatic>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(DeviceState* st, const u32x4* __restrict__ q,
+                                                            const u32x4* __restrict__ k, const u32x4* __restrict__ v,
+                                                            int64_t n_chunks, u32x2* __restrict__ q8,
+                                                            u32x2* __restrict__ k8, u32x2* __restrict__ v8) {
+    const int t = blockIdx.y;
+    float inv;
+    if constexpr (kStatic) {
+        const float eff = st->static_eff[t];
+        float d;
+        scales_from_amax(eff, &d, &inv);
+        // The static factors do not depend on the data: workgroup 0 records
+        // them; every workgroup derives the same value from static_eff.
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            st->amax_eff[t] = eff;
+            st->descale[t] = d;
+            st->inv[t] = inv;
+        }
+    } else {
+        inv = st->inv[t];
+    }
+    const u32x4* __restrict__ src = t == 0 ? q : (t == 1 ? k : v);
+    u32x2* __restrict__ dst = t == 0 ? q8 : (t == 1 ? k8 : v8);
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    for (; i + 3 * stride < n_chunks; i += 4 * stride) {
+        const u32x4 a = __builtin_nontemporal_load(src + i);
+        const u32x4 b = __builtin_nontemporal_load(src + i + stride);
+        const u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
+        const u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
+        __builtin_nontemporal_store(quantize8(a, inv), dst + i);
+        __builtin_nontemporal_store(quantize8(b, inv), dst + i + stride);
+        __builtin_nontemporal_store(quantize8(c, inv), dst + i + 2 * stride);
+        __builtin_nontemporal_store(quantize8(d, inv), dst + i + 3 * stride);
+    }
+    for (; i < n_chunks; i += stride) __builtin_nontemporal_store(quantize8(__builtin_nontemporal_load(src + i), inv), dst + i);
+}
+
+int grid_for(int64_t n_chunks, int64_t chunks_per_thread, int cap) {
+    int64_t g = (n_chunks + kThreads * chunks_per_thread - 1) / (kThreads * chunks_per_thread);
+    if (g < 1) g = 1;
+    if (g > cap) g = cap;
+    return (int)g;
+}
+
+}  // namespace
+
+hipError_t launch_init_state(DeviceState* st, int history_len, const float static_eff[3], hipStream_t s) {
+    init_state_kernel<<<1, 64, 0, s>>>(st, history_len, static_eff[0], static_eff[1], static_eff[2]);
+    return hipGetLastError();
+}
+
+// n: elements per tensor (a multiple of 128, so of 8).
+hipError_t launch_quantize_dynamic(DeviceState* st, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   int64_t n, uint8_t* q8, uint8_t* k8, uint8_t* v8, hipStream_t s) {
+    const int64_t chunks = n / 8;
+    const int ga = grid_for(chunks, 8, kMaxPartials);
+    amax_partial_kernel<<<dim3(ga, 3), kThreads, 0, s>>>((const u32x4*)q, (const u32x4*)k, (const u32x4*)v, chunks,
+                                                         &st->partial[0][0]);
+    finalize_dynamic_kernel<<<1, kThreads, 0, s>>>(st, ga);
+    const int gq = grid_for(chunks, 4, 2048);
+    quantize_kernel<false><<<dim3(gq, 3), kThreads, 0, s>>>(st, (const u32x4*)q, (const u32x4*)k, (const u32x4*)v,
+                                                           chunks, (u32x2*)q8, (u32x2*)k8, (u32x2*)v8);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_static(DeviceState* st, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                  int64_t n, uint8_t* q8, uint8_t* k8, uint8_t* v8, hipStream_t s) {
+    const int64_t chunks = n / 8;
+    const int gq = grid_for(chunks, 4, 2048);
+    quantize_kernel<true><<<dim3(gq, 3), kThreads, 0, s>>>(st, (const u32x4*)q, (const u32x4*)k, (const u32x4*)v,
+                                                          chunks, (u32x2*)q8, (u32x2*)k8, (u32x2*)v8);
+    return hipGetLastError();
+}
+
+}  // namespace qfa

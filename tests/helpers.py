@@ -1,0 +1,57 @@
+"""Test-side helpers: host copies of device tensors and the attention tolerance.
+
+Tolerance (floating point, attention output): with ``r`` the oracle's float64
+output and ``g`` the kernel's bf16 output, ``e = |g - r| / max(1, |r|)``;
+pass iff ``max(e) <= 3e-2`` and ``mean(e) <= 3e-3``.  That is the absolute
+check for unit-scale outputs and the same check after scaling each larger
+output to unit size (outputs reach ~100 where V has x20-x30 outliers, where
+bf16 rounding alone exceeds 3e-2 in absolute terms).
+"""
+
+import sys
+
+import numpy as np
+import torch
+
+TOL_MAX = 3e-2
+TOL_MEAN = 3e-3
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def bf16_to_f32(t: torch.Tensor) -> np.ndarray:
+    """bf16 tensor (any device) -> float32 numpy array with the same values."""
+    return t.detach().to("cpu").float().numpy()
+
+
+def codes(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu").numpy()
+
+
+def attn_errors(g: np.ndarray, r: np.ndarray, scale=None):
+    """(max e, mean e) with e = |g - r| / max(1, scale); scale defaults to |r|."""
+    g = np.asarray(g, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    s = np.abs(r) if scale is None else np.asarray(scale, dtype=np.float64)
+    e = np.abs(g - r) / np.maximum(1.0, s)
+    return float(e.max()), float(e.mean())
+
+
+def assert_attn_close(g, r, what="", mag=None):
+    """Check the kernel's output g against the oracle's r (see the module docstring).
+
+    ``mag`` is the oracle's M = P|V| for the same elements; when given it is
+    the element scale, otherwise |r| is.
+    """
+    mx_r, mean_r = attn_errors(g, r)
+    msg = f"  {what}: e/max(1,|r|) max {mx_r:.3e} mean {mean_r:.3e}"
+    mx, mean = mx_r, mean_r
+    if mag is not None:
+        mx, mean = attn_errors(g, r, mag)
+        msg += f" | e/max(1,P|V|) max {mx:.3e} mean {mean:.3e}"
+    log(msg)
+    assert np.isfinite(g).all(), f"{what}: non-finite output"
+    assert mx <= TOL_MAX and mean <= TOL_MEAN, f"{what}: max e {mx:.3e}, mean e {mean:.3e}"

@@ -1,0 +1,141 @@
+"""C ABI checks that need no GPU: exported symbols and argument validation.
+
+Every entry point validates its arguments on the host before any HIP call,
+so each error status here is reached without touching a device.  The fake
+device pointers are never dereferenced.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import quantized_flash_attn_amd as qfa
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "qfa.h")
+lib = qfa.raw_library()
+FAKE = 0x10000          # 16-byte aligned, never dereferenced
+MISALIGNED = 0x10004
+
+OK, NULL, SHAPE, UNSUP, ALIGN, MODE, NO_STATIC, VALUE, STATE = 0, 1, 2, 3, 4, 5, 6, 7, 8
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qfa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    declared = header_functions()
+    assert len(declared) == 9, declared
+    out = subprocess.run(["nm", "-D", "--defined-only", qfa.library_path()], stdout=subprocess.PIPE, text=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    missing = [f for f in declared if f not in exported]
+    assert not missing, missing
+    assert set(declared) == set(qfa.EXPORTS)
+
+
+def test_state_bytes_and_status_strings():
+    assert 256 <= qfa.scale_state_bytes() <= 64 * 1024
+    for s in range(11):
+        assert lib.qfa_status_string(s)
+    assert lib.qfa_status_string(99) == b"unknown status"
+
+
+def _init(handle, buf=FAKE, hist=16, static=None, margin=1.5):
+    sa = None if static is None else (ctypes.c_float * 3)(*static)
+    return lib.qfa_init_scale_state(handle, buf, hist, sa, ctypes.c_float(margin), None)
+
+
+def test_init_validation():
+    h = qfa._State()
+    assert _init(None) == NULL
+    assert _init(ctypes.byref(h), buf=None) == NULL
+    assert _init(ctypes.byref(h), buf=MISALIGNED) == ALIGN
+    for hist in (0, 17, -3):
+        assert _init(ctypes.byref(h), hist=hist) == VALUE
+    for bad in ([1.0, 0.0, 1.0], [1.0, -2.0, 3.0], [float("nan"), 1.0, 1.0], [float("inf"), 1.0, 1.0]):
+        assert _init(ctypes.byref(h), static=bad) == VALUE
+    assert _init(ctypes.byref(h), static=[3e38, 1.0, 1.0], margin=1.5) == VALUE   # product overflows
+    for m in (0.0, -1.5, float("inf"), float("nan")):
+        assert _init(ctypes.byref(h), static=[1.0, 1.0, 1.0], margin=m) == VALUE
+    assert h.magic == 0                      # nothing was initialised
+    assert b"history_len" in lib.qfa_last_error() or lib.qfa_last_error()
+
+
+def _handle(has_static=0, magic=0x31414651):
+    h = qfa._State()
+    h.magic = magic
+    h.history_len = 16
+    h.has_static = has_static
+    h.device = FAKE
+    return h
+
+
+def _quant(h, mode=0, ptrs=(FAKE,) * 6, T=8, H=2, D=128):
+    q, k, v, q8, k8, v8 = ptrs
+    return lib.qfa_quantize_qkv(h, mode, q, k, v, T, H, D, q8, k8, v8, None)
+
+
+def test_quantize_validation():
+    assert _quant(None) == NULL
+    assert _quant(ctypes.byref(_handle(magic=0))) == STATE
+    h = _handle()
+    assert _quant(ctypes.byref(h), mode=2) == MODE
+    assert _quant(ctypes.byref(h), mode=-1) == MODE
+    assert _quant(ctypes.byref(h), mode=1) == NO_STATIC
+    assert _quant(ctypes.byref(h), D=64) == UNSUP
+    assert _quant(ctypes.byref(h), H=0) == SHAPE
+    assert _quant(ctypes.byref(h), T=-1) == SHAPE
+    assert _quant(ctypes.byref(h), T=1 << 40) == SHAPE
+    for i in range(6):
+        p = [FAKE] * 6
+        p[i] = None
+        assert _quant(ctypes.byref(h), ptrs=tuple(p)) == NULL
+        p[i] = MISALIGNED
+        assert _quant(ctypes.byref(h), ptrs=tuple(p)) == ALIGN
+    hs = _handle(has_static=1)
+    assert _quant(ctypes.byref(hs), mode=1, D=100) == UNSUP
+
+
+def _attn(q8=FAKE, k8=FAKE, v8=FAKE, sc=FAKE, cu=FAKE, B=1, T=8, H=2, D=128, out=FAKE):
+    return lib.qfa_fp8_varlen_attn(q8, k8, v8, sc, cu, B, T, H, D, out, None)
+
+
+def test_attention_validation():
+    assert _attn(D=64) == UNSUP
+    assert _attn(H=0) == SHAPE
+    assert _attn(T=-5) == SHAPE
+    assert _attn(B=0) == SHAPE
+    assert _attn(T=1 << 31, H=1) == SHAPE
+    assert _attn(sc=None) == NULL
+    assert _attn(cu=None) == NULL
+    for name in ("q8", "k8", "v8", "out"):
+        assert _attn(**{name: None}) == NULL
+        assert _attn(**{name: MISALIGNED}) == ALIGN
+    assert _attn(sc=FAKE + 2) == ALIGN
+    assert _attn(cu=FAKE + 1) == ALIGN
+
+
+def test_other_entry_points_validation():
+    assert lib.qfa_descale_ptr(None) is None
+    assert lib.qfa_descale_ptr(ctypes.byref(_handle(magic=0))) is None
+    assert lib.qfa_read_scale_state(None, None, None) == NULL
+    snap = qfa._Snapshot()
+    assert lib.qfa_read_scale_state(ctypes.byref(_handle(magic=0)), ctypes.byref(snap), None) == STATE
+    assert lib.qfa_check_cu_seqlens(None, 1, 8, None) == NULL
+    assert lib.qfa_check_cu_seqlens(FAKE, 0, 8, None) == SHAPE
+    assert lib.qfa_check_cu_seqlens(FAKE, 1, -1, None) == SHAPE
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros((4, 2, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        qfa.quantize_qkv(None, "dynamic", x, x, x)
+    c = torch.zeros((4, 2, 128), dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        qfa.fp8_varlen_attn(c, c, c, torch.ones(3), torch.tensor([0, 4], dtype=torch.int32), 2)

@@ -1,0 +1,198 @@
+"""GPU parity of the varlen FP8 attention against the oracle.
+
+The GPU runs the whole path through the C ABI (quantize, then attention on
+its own codes and scales); the oracle runs its own path (quantize, then
+float64 attention) on host copies of the same bf16 inputs.  Codes must agree
+bit-exactly; outputs within the tolerance stated in tests/helpers.py.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_flash_attn_amd as qfa
+from helpers import assert_attn_close, bf16_to_f32, codes, log
+from workloads import WORKLOADS, cu_seqlens_tensor, make_qkv, random_qkv
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def gpu_path(q, k, v, seqlens, state=None, mode="dynamic"):
+    st = state if state is not None else qfa.init_scale_state(DEV)
+    q8, k8, v8 = qfa.quantize_qkv(st, mode, q, k, v)
+    cu = cu_seqlens_tensor(seqlens, DEV)
+    qfa.check_cu_seqlens(cu, q.shape[0])
+    out = qfa.fp8_varlen_attn(q8, k8, v8, qfa.descale(st), cu, q.shape[1])
+    return (q8, k8, v8), out, st
+
+
+def oracle_path(q, k, v, seqlens, ost=None, mode="dynamic"):
+    ost = ost if ost is not None else oracle.ScaleState()
+    qh, kh, vh = (bf16_to_f32(t) for t in (q, k, v))
+    q8, k8, v8, descale, _ = oracle.quantize_qkv(ost, mode, qh, kh, vh)
+    cu = np.concatenate([[0], np.cumsum(seqlens)])
+    return (q8, k8, v8), oracle.attention(q8, k8, v8, descale, cu, magnitude=True), descale
+
+
+@pytest.mark.parametrize("seqlens,H,sigma,outliers", [
+    ([1], 1, 1.0, 0.0),
+    ([7], 2, 1.0, 0.0),
+    ([128], 2, 2.0, 0.0),
+    ([129], 3, 1.0, 0.001),
+    ([255, 1, 300], 2, 3.0, 0.001),
+    ([0, 513, 0, 17], 2, 1.5, 0.0),
+    ([1000, 24, 389], 3, 2.5, 0.002),
+    ([2, 3, 5, 7, 11, 13, 17, 19, 23, 29, 31, 37, 41, 43, 47, 53], 1, 1.0, 0.0),
+])
+def test_small_ragged(seqlens, H, sigma, outliers):
+    log(f"seqlens={seqlens} H={H} sigma={sigma}")
+    q, k, v = random_qkv(seqlens, H, seed=sum(seqlens) * 7 + H, device=DEV, sigma=sigma, outlier_p=outliers,
+                         outlier_scale=20.0)
+    gcodes, out, _ = gpu_path(q, k, v, seqlens)
+    ocodes, (ref, mag), _ = oracle_path(q, k, v, seqlens)
+    for g, o in zip(gcodes, ocodes):
+        assert np.array_equal(codes(g), o)
+    assert_attn_close(bf16_to_f32(out), ref, f"seqlens {seqlens}", mag=mag)
+
+
+def test_distinct_tensor_scales():
+    """Very different Q, K, V ranges: the three scales must each go to the right place."""
+    seqlens = [200, 77]
+    q, k, v = random_qkv(seqlens, 2, seed=5, device=DEV)
+    q, k, v = q * 0.01, k * 30.0, v * 100.0
+    _, out, _ = gpu_path(q, k, v, seqlens)
+    _, (ref, mag), _ = oracle_path(q, k, v, seqlens)
+    assert_attn_close(bf16_to_f32(out), ref, "distinct scales", mag=mag)
+
+
+def test_static_scales_attention():
+    seqlens = [300, 129]
+    q, k, v = random_qkv(seqlens, 2, seed=9, device=DEV, sigma=2.0)
+    sa = [5.0, 7.0, 3.0]
+    st = qfa.init_scale_state(DEV, static_amax=sa, margin=1.5)
+    _, out, _ = gpu_path(q, k, v, seqlens, state=st, mode="static")
+    _, (ref, mag), _ = oracle_path(q, k, v, seqlens, ost=oracle.ScaleState(static_amax=sa, margin=1.5), mode="static")
+    assert_attn_close(bf16_to_f32(out), ref, "static", mag=mag)
+
+
+def test_one_token_sequence_returns_v_row():
+    seqlens = [5, 1, 9, 1]
+    q, k, v = random_qkv(seqlens, 2, seed=13, device=DEV, sigma=2.0)
+    (q8, k8, v8), out, st = gpu_path(q, k, v, seqlens)
+    s_v = np.float32(qfa.read_scale_state(st)["descale"][2])
+    for row in (5, 15):
+        want = (oracle.decode(codes(v8)[row]).astype(np.float32) * s_v).astype(np.float32)
+        want_bf16 = torch.from_numpy(want).to(torch.bfloat16).float().numpy()
+        got = bf16_to_f32(out[row])
+        ulp = np.abs(want_bf16) * 2.0 ** -7 + 1e-30
+        assert np.all(np.abs(got - want_bf16) <= ulp), row
+        log(f"  row {row}: {np.count_nonzero(got == want_bf16)} of {got.size} bit-equal")
+
+
+def test_identical_keys_give_mean_of_v():
+    seqlens = [300]
+    q, k, v = random_qkv(seqlens, 2, seed=17, device=DEV)
+    k = k[:1].expand_as(k).contiguous()
+    (_, _, v8), out, st = gpu_path(q, k, v, seqlens)
+    s_v = qfa.read_scale_state(st)["descale"][2]
+    mean_v = (oracle.decode(codes(v8)) * s_v).mean(axis=0)
+    assert_attn_close(bf16_to_f32(out), np.broadcast_to(mean_v, out.shape), "identical keys")
+
+
+def test_no_leakage_and_determinism():
+    seqlens = [300, 129, 64, 500]
+    q, k, v = random_qkv(seqlens, 2, seed=19, device=DEV)
+    st = qfa.init_scale_state(DEV, static_amax=[8.0, 8.0, 8.0], margin=1.0)   # fixed scales for both runs
+    (q8, k8, v8), out1, _ = gpu_path(q, k, v, seqlens, state=st, mode="static")
+    out2 = qfa.fp8_varlen_attn(q8, k8, v8, qfa.descale(st), cu_seqlens_tensor(seqlens, DEV), 2)
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16)), "not deterministic"
+    cu = np.concatenate([[0], np.cumsum(seqlens)])
+    k2, v2 = k.clone(), v.clone()
+    k2[cu[1]:cu[2]] = torch.randn_like(k2[cu[1]:cu[2]].float()).to(torch.bfloat16) * 5
+    v2[cu[1]:cu[2]] = torch.randn_like(v2[cu[1]:cu[2]].float()).to(torch.bfloat16) * 5
+    _, out3, _ = gpu_path(q, k2, v2, seqlens, state=st, mode="static")
+    for b in (0, 2, 3):
+        assert torch.equal(out1[cu[b]:cu[b + 1]].view(torch.int16), out3[cu[b]:cu[b + 1]].view(torch.int16)), b
+    assert not torch.equal(out1[cu[1]:cu[2]], out3[cu[1]:cu[2]])
+
+
+def test_static_without_scales_is_refused():
+    st = qfa.init_scale_state(DEV)
+    x = torch.zeros((4, 1, 128), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(qfa.QfaError) as ei:
+        qfa.quantize_qkv(st, "static", x, x, x)
+    assert ei.value.status == 6
+
+
+def _sample_rows(w):
+    """Rows checked at full size: all rows, or seeded samples of the workload's ranges."""
+    if not w.oracle_rows:
+        if w.total_tokens <= 2304:
+            return np.arange(w.total_tokens)
+        step = max(1, w.total_tokens // 1024)
+        return np.unique(np.concatenate([np.arange(0, w.total_tokens, step),
+                                         np.arange(w.total_tokens - 128, w.total_tokens)]))
+    rng = np.random.default_rng(w.index)
+    parts = []
+    for lo, hi in w.oracle_rows:
+        n = hi - lo
+        if n <= 2304:
+            parts.append(np.arange(lo, hi))
+        else:
+            parts.append(np.sort(rng.choice(np.arange(lo, hi), size=384, replace=False)))
+            parts.append(np.arange(hi - 128, hi))          # the range's ragged final tile
+    return np.unique(np.concatenate(parts))
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("widx", [1, 2, 3, 4, 5])
+def test_workload_attention(widx):
+    """Full-size workloads in the benchmark's launch configuration; sampled rows vs the oracle."""
+    w = WORKLOADS[widx]
+    mode = w.modes[0]
+    log(f"workload {widx} ({w.name}), mode {mode}")
+    if mode == "static":
+        cal = make_qkv(w, 0, device=DEV, calibration=True)
+        sa = [oracle.amax(bf16_to_f32(t)) for t in cal]
+        del cal
+        st = qfa.init_scale_state(DEV, static_amax=sa, margin=1.5)
+        ost = oracle.ScaleState(static_amax=sa, margin=1.5)
+    else:
+        st = qfa.init_scale_state(DEV)
+        ost = oracle.ScaleState()
+    for fwd in range(w.forwards):
+        xs = make_qkv(w, fwd, device=DEV)
+        gq8, gk8, gv8 = qfa.quantize_qkv(st, mode, *xs)
+        if mode == "dynamic":
+            _, inv = ost.forward_dynamic([oracle.amax(bf16_to_f32(x)) for x in xs])
+        else:
+            _, inv = ost.forward_static()
+        if fwd < w.forwards - 1:
+            del xs, gq8, gk8, gv8
+    cu_list = w.cu_seqlens
+    out = qfa.fp8_varlen_attn(gq8, gk8, gv8, qfa.descale(st), cu_seqlens_tensor(w.seqlens, DEV), w.num_heads)
+    torch.cuda.synchronize()
+    rows = _sample_rows(w)
+    cu = np.array(cu_list)
+    seqs = np.unique(np.searchsorted(cu, rows, side="right") - 1)
+    log(f"  checking {rows.size} rows in sequences {seqs.tolist()}")
+    # oracle codes for the checked query rows and the keys/values of their sequences
+    q, k, v = xs
+    rows_t = torch.from_numpy(rows).to(DEV)
+    oq8 = np.zeros((w.total_tokens, w.num_heads, 128), np.uint8)
+    ok8 = np.zeros_like(oq8)
+    ov8 = np.zeros_like(oq8)
+    oq8[rows] = oracle.quantize(bf16_to_f32(q[rows_t]), inv[0])
+    assert np.array_equal(codes(gq8[rows_t]), oq8[rows])
+    for b in seqs:
+        lo, hi = cu[b], cu[b + 1]
+        ok8[lo:hi] = oracle.quantize(bf16_to_f32(k[lo:hi]), inv[1])
+        ov8[lo:hi] = oracle.quantize(bf16_to_f32(v[lo:hi]), inv[2])
+        assert np.array_equal(codes(gk8[lo:hi]), ok8[lo:hi])
+        assert np.array_equal(codes(gv8[lo:hi]), ov8[lo:hi])
+    ref, mag = oracle.attention_rows(oq8, ok8, ov8, ost.descale, cu, rows, magnitude=True)
+    got = bf16_to_f32(out[rows_t])
+    assert_attn_close(got, ref, f"workload {widx}", mag=mag)

@@ -186,3 +186,22 @@ def test_cu_seqlens_validation():
     for bad in ([0, 7], [1, 8], [0, 5, 3, 8], [0]):
         with pytest.raises(ValueError):
             attention(q8, k8, v8, descale, bad)
+
+
+def test_magnitude_scale():
+    """M = P|V|: at least |O| everywhere, equal to O when V >= 0, 1 when V = 1."""
+    seqlens = [40, 9]
+    _, (q8, k8, v8), descale = _quant(seqlens, 2, seed=101, sigma=2.0)
+    cu = _cu(seqlens)
+    out, mag = attention(q8, k8, v8, descale, cu, magnitude=True)
+    assert np.array_equal(out, attention(q8, k8, v8, descale, cu))
+    assert np.all(mag >= np.abs(out) - 1e-12)
+    pos = v8 & 0x7F                                       # clear sign bits: V >= 0
+    out_p, mag_p = attention(q8, k8, pos, descale, cu, magnitude=True)
+    assert np.abs(mag_p - out_p).max() <= 1e-12
+    ones = np.full(q8.shape, 0x38, dtype=np.uint8)
+    _, mag_1 = attention(q8, k8, ones, np.array([descale[0], descale[1], 1.0], np.float32), cu, magnitude=True)
+    assert np.abs(mag_1 - 1.0).max() <= 1e-12
+    rows = np.array([0, 39, 40, 48])
+    o_r, m_r = attention_rows(q8, k8, v8, descale, cu, rows, magnitude=True)
+    assert np.abs(o_r - out[rows]).max() <= 1e-12 and np.abs(m_r - mag[rows]).max() <= 1e-12

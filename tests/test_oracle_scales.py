@@ -148,6 +148,8 @@ def test_static_validation():
         with pytest.raises(ValueError):
             ScaleState(static_amax=[1.0, 1.0, 1.0], margin=m)
     with pytest.raises(ValueError):
+        ScaleState(static_amax=[3e38, 1.0, 1.0], margin=1.5)     # product overflows float32
+    with pytest.raises(ValueError):
         ScaleState().forward_static()
 
 
