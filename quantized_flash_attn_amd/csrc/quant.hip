@@ -105,34 +105,37 @@ __global__ __launch_bounds__(kThreads) void amax_partial_kernel(const u32x4* __r
     }
 }
 
-__global__ __launch_bounds__(kThreads) void finalize_dynamic_kernel(DeviceState* st, int n_partials) {
-    __shared__ uint32_t red[3][kThreads / 64];
-    for (int t = 0; t < 3; ++t) {
-        uint32_t m = 0;
-        for (int j = threadIdx.x; j < n_partials; j += kThreads) m = max(m, st->partial[t][j]);
-        m = wave_max_u32(m);
-        if ((threadIdx.x & 63) == 0) red[t][threadIdx.x >> 6] = m;
-    }
-    __syncthreads();
-    if (threadIdx.x != 0) return;
+// One workgroup of three waves: wave t reduces tensor t's partials; lanes
+// 0..15 of that wave hold the ring slots, so the push and the ring maximum
+// are register and cross-lane work with no dependent memory round trips.
+// All shared state is read before the barrier and written after it; every
+// state field has exactly one writing lane.
+constexpr int kFinalizeThreads = 192;
+__global__ __launch_bounds__(kFinalizeThreads) void finalize_dynamic_kernel(DeviceState* st, int n_partials) {
+    const int t = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    uint32_t m = 0;
+    for (int j = lane; j < n_partials; j += 64) m = max(m, st->partial[t][j]);
+    m = wave_max_u32(m);
+    const float amax = __uint_as_float(m << 16);
     const int cursor = st->cursor;
     const int hist = st->history_len;
     const int slot = cursor % hist;
-    for (int t = 0; t < 3; ++t) {
-        uint32_t bits = red[t][0];
-        for (int w = 1; w < kThreads / 64; ++w) bits = max(bits, red[t][w]);
-        const float amax = __uint_as_float(bits << 16);
-        st->ring[t][slot] = amax;
+    float r = lane < hist ? st->ring[t][lane] : 0.0f;
+    __syncthreads();
+    if (lane == slot) r = amax;
+    float eff = r;
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) eff = fmaxf(eff, __shfl_xor(eff, off));  // max over lanes 0..15
+    if (lane == slot) st->ring[t][slot] = amax;
+    if (lane == 0) {
         st->amax_observed[t] = amax;
-        float eff = 0.0f;
-        for (int j = 0; j < hist; ++j) eff = fmaxf(eff, st->ring[t][j]);
         st->amax_eff[t] = eff;
         float d, i;
         scales_from_amax(eff, &d, &i);
         st->descale[t] = d;
         st->inv[t] = i;
+        if (t == 0) st->cursor = cursor + 1;
     }
-    st->cursor = cursor + 1;
 }
 
 // 8 bf16 values -> 8 E4M3 codes: fp32 multiply (RNE), clamp to +-448 (the
@@ -217,7 +220,7 @@ hipError_t launch_quantize_dynamic(DeviceState* st, const uint16_t* q, const uin
     const int ga = grid_for(chunks, 8, kMaxPartials);
     amax_partial_kernel<<<dim3(ga, 3), kThreads, 0, s>>>((const u32x4*)q, (const u32x4*)k, (const u32x4*)v, chunks,
                                                          &st->partial[0][0]);
-    finalize_dynamic_kernel<<<1, kThreads, 0, s>>>(st, ga);
+    finalize_dynamic_kernel<<<1, kFinalizeThreads, 0, s>>>(st, ga);
     const int gq = grid_for(chunks, 4, 2048);
     quantize_kernel<false><<<dim3(gq, 3), kThreads, 0, s>>>(st, (const u32x4*)q, (const u32x4*)k, (const u32x4*)v,
                                                            chunks, (u32x2*)q8, (u32x2*)k8, (u32x2*)v8);
