@@ -3,8 +3,8 @@
 "FP8 vision encoder attention" (Requirements) runs FP8 varlen attention with
 per-tensor scales over packed variable-length image batches; "FP8 ViT
 Encoder Attention" (intro, note) applies it to ViT encoder attention of
-single- and multi-image requests.  Readings where the pages are silent (listed
-in the design doc): non-causal attention, softmax scale ``1/sqrt(head_dim)``,
+single- and multi-image requests.  Readings taken where the pages are silent:
+non-causal attention, softmax scale ``1/sqrt(head_dim)``,
 attention only within each sequence ``[cu_seqlens[b], cu_seqlens[b+1])``,
 tensors laid out ``[tokens, heads, head_dim]``.
 

@@ -13,7 +13,7 @@ Pages (cited by title and section):
   multiplied by a save margin whose default is 1.5; static scales remove the
   dynamic work.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 
 * One buffer per tensor (Q, K, V); unfilled slots start at 0, so the maximum
   over all slots is the maximum over the filled ones.
