@@ -36,7 +36,31 @@ def parse():
     p.add_argument("--sets", type=int, default=4, help="input sets rotated through (defeats the 256 MB cache)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=256, help="query rows of the oracle's attention sample")
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="instead of the benchmark, time a plain device copy of this many MiB (the known-size "
+                        "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
+
+
+def copy_calibration(mib, steps):
+    """Plain device-to-device copy of a known size; prints one JSON line."""
+    import torch
+
+    dev = torch.device("cuda", 0)
+    n = mib * 1024 * 1024
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": round(ms, 4),
+                      "gbs_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
 def cpu_baseline(w, xs_host, descale_inv, rows):
@@ -84,8 +108,32 @@ def cpu_baseline(w, xs_host, descale_inv, rows):
     }
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_seq8192_h16.json")
+ATTN_SRC = os.path.join(ROOT, "quantized_flash_attn_amd", "csrc", "attn.hip")
+
+
+def measured_traffic(workload_index):
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary, or None.
+
+    Only valid for the workload the counters were taken on and while the kernel source is
+    unchanged since (its sha256 is recorded next to the counts)."""
+    import hashlib
+
+    if workload_index != 3 or not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    with open(ATTN_SRC, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec["sources_sha256"]["attn.hip"]:
+            return None
+    return rec["kernels"]["attn_fwd_kernel"]["traffic_bytes"]
+
+
 def main():
     args = parse()
+    if args.copy_calibration_mib > 0:
+        copy_calibration(args.copy_calibration_mib, args.steps)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
@@ -163,7 +211,7 @@ def main():
         "quantize_dynamic": {"ms": round(ms_quant, 4), "algorithmic_bytes": quant_bytes, "gbs": round(quant_gbs, 1),
                              "frac_hbm_peak": round(quant_gbs / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(attn_tflops / FP8_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(attn_tflops / FP8_PEAK_TFLOPS, 4), "traffic": measured_traffic(args.workload),
                      "kernel": "attn_fwd_kernel", "flop_per_launch": flop},
         "wall_s_timed_region": round(wall, 4),
     }

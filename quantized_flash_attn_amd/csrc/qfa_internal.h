@@ -11,7 +11,7 @@ namespace qfa {
 
 // Partial amax results one forward may write per tensor (the amax grid is
 // capped to this many workgroups per tensor).
-constexpr int kMaxPartials = 1024;
+constexpr int kMaxPartials = 256;
 
 // Device-resident scale state of one attention layer (the caller's buffer).
 // Tensor index t: 0 = Q, 1 = K, 2 = V.
@@ -23,6 +23,7 @@ struct DeviceState {
     float inv[3];                     // quantization factors
     float static_eff[3];              // fp32(static_amax * margin)
     int32_t cursor;                   // dynamic forwards so far
+    int32_t cursor_snap;              // cursor as the current forward's amax pass found it
     int32_t history_len;              // 1..16
     alignas(16) uint32_t partial[3][kMaxPartials];  // per-workgroup max of |bf16| bit patterns
 };

@@ -8,12 +8,16 @@
 // times a margin.  Quantization ("FP8 ViT Encoder Attention", intro) turns
 // Q/K/V into FP8 before the attention call.
 //
-// Kernels (all HBM-streaming except the single-workgroup finalize):
+// Kernels (both HBM-streaming):
 //   amax_partial_kernel    grid (P, 3): max of |x| as bf16 bit patterns,
-//                          one partial per workgroup, no atomics
-//   finalize_dynamic_kernel  one workgroup: reduce partials, push the ring,
-//                          cursor++, compute descale and inv (single writer)
-//   quantize_kernel        grid (G, 3): x * inv -> clamp +-448 -> E4M3 (RNE)
+//                          one partial per workgroup, no atomics; workgroup
+//                          (0, 0) also snapshots the ring cursor
+//   quantize_kernel        grid (G, 3): x * inv -> clamp +-448 -> E4M3 (RNE).
+//                          Dynamic mode: every workgroup first reduces its
+//                          tensor's partials and derives the forward's scale
+//                          from the ring itself (all workgroups compute the
+//                          same value); workgroup (0, t) is the only writer of
+//                          ring slot, cursor and scales.  No atomics.
 
 #include "qfa_internal.h"
 
@@ -76,8 +80,12 @@ __device__ inline uint32_t max_abs_bits(u32x4 w, uint32_t m) {
 
 __global__ __launch_bounds__(kThreads) void amax_partial_kernel(const u32x4* __restrict__ q, const u32x4* __restrict__ k,
                                                                 const u32x4* __restrict__ v, int64_t n_chunks,
-                                                                uint32_t* __restrict__ partial) {
+                                                                DeviceState* st) {
     const int t = blockIdx.y;
+    uint32_t* __restrict__ partial = &st->partial[0][0];
+    // The ring cursor as this forward finds it; the quantize kernel reads the
+    // snapshot while its workgroup (0, 0) advances the cursor itself.
+    if (blockIdx.x == 0 && t == 0 && threadIdx.x == 0) st->cursor_snap = st->cursor;
     const u32x4* __restrict__ src = t == 0 ? q : (t == 1 ? k : v);
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -105,37 +113,60 @@ __global__ __launch_bounds__(kThreads) void amax_partial_kernel(const u32x4* __r
     }
 }
 
-// One workgroup of three waves: wave t reduces tensor t's partials; lanes
-// 0..15 of that wave hold the ring slots, so the push and the ring maximum
-// are register and cross-lane work with no dependent memory round trips.
-// All shared state is read before the barrier and written after it; every
-// state field has exactly one writing lane.
-constexpr int kFinalizeThreads = 192;
-__global__ __launch_bounds__(kFinalizeThreads) void finalize_dynamic_kernel(DeviceState* st, int n_partials) {
-    const int t = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    uint32_t m = 0;
-    for (int j = lane; j < n_partials; j += 64) m = max(m, st->partial[t][j]);
-    m = wave_max_u32(m);
-    const float amax = __uint_as_float(m << 16);
-    const int cursor = st->cursor;
+// The forward's scale for tensor t, derived inside every quantize workgroup
+// from state written before this kernel started (the amax partials, the
+// ring and the cursor snapshot), so all workgroups agree without
+// synchronising.  amax_t = max of the partials; the ring's slot
+// cursor % history_len receives amax_t, so the effective amax is the maximum
+// of amax_t and the other slots (the slot being replaced is excluded: its
+// old value leaves the window).  Workgroup (0, t) writes the slot, the
+// scales and (t = 0) the incremented cursor; nobody else reads those fields
+// during this kernel, and its readers exclude the slot, so there is no race.
+__device__ float dynamic_inv(DeviceState* st, int t, int n_partials) {
+    __shared__ uint32_t red[kThreads / 64];
+    __shared__ float sh_inv;
+    const int lane = threadIdx.x & 63;
+    // This thread's partials (indices past the last are clamped to it: a
+    // repeated value does not change the maximum), all loaded before use.
+    constexpr int kPerThread = kMaxPartials / kThreads;
+    uint32_t v[kPerThread];
+#pragma unroll
+    for (int r = 0; r < kPerThread; ++r) v[r] = st->partial[t][min((int)threadIdx.x + kThreads * r, n_partials - 1)];
+    // Ring slots other than the one being replaced, one per lane.
+    const int cursor = st->cursor_snap;
     const int hist = st->history_len;
     const int slot = cursor % hist;
-    float r = lane < hist ? st->ring[t][lane] : 0.0f;
-    __syncthreads();
-    if (lane == slot) r = amax;
-    float eff = r;
+    const float rv = (lane < hist && lane != slot) ? st->ring[t][lane] : 0.0f;
+    uint32_t m = 0;
 #pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) eff = fmaxf(eff, __shfl_xor(eff, off));  // max over lanes 0..15
-    if (lane == slot) st->ring[t][slot] = amax;
-    if (lane == 0) {
-        st->amax_observed[t] = amax;
-        st->amax_eff[t] = eff;
-        float d, i;
-        scales_from_amax(eff, &d, &i);
-        st->descale[t] = d;
-        st->inv[t] = i;
-        if (t == 0) st->cursor = cursor + 1;
+    for (int r = 0; r < kPerThread; ++r) m = max(m, v[r]);
+    m = wave_max_u32(m);
+    if (lane == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        uint32_t bits = red[0];
+#pragma unroll
+        for (int w = 1; w < kThreads / 64; ++w) bits = max(bits, red[w]);
+        const float amax = __uint_as_float(bits << 16);
+        float eff = fmaxf(amax, rv);
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) eff = fmaxf(eff, __shfl_xor(eff, off));  // max over lanes 0..15
+        if (lane == 0) {
+            float d, i;
+            scales_from_amax(eff, &d, &i);
+            sh_inv = i;
+            if (blockIdx.x == 0) {
+                st->ring[t][slot] = amax;
+                st->amax_observed[t] = amax;
+                st->amax_eff[t] = eff;
+                st->descale[t] = d;
+                st->inv[t] = i;
+                if (t == 0) st->cursor = cursor + 1;
+            }
+        }
     }
+    __syncthreads();
+    return sh_inv;
 }
 
 // 8 bf16 values -> 8 E4M3 codes: fp32 multiply (RNE), clamp to +-448 (the
@@ -165,7 +196,8 @@ template <bool kStatic>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(DeviceState* st, const u32x4* __restrict__ q,
                                                             const u32x4* __restrict__ k, const u32x4* __restrict__ v,
                                                             int64_t n_chunks, u32x2* __restrict__ q8,
-                                                            u32x2* __restrict__ k8, u32x2* __restrict__ v8) {
+                                                            u32x2* __restrict__ k8, u32x2* __restrict__ v8,
+                                                            int n_partials) {
     const int t = blockIdx.y;
     float inv;
     if constexpr (kStatic) {
@@ -180,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(DeviceState* st, con
             st->inv[t] = inv;
         }
     } else {
-        inv = st->inv[t];
+        inv = dynamic_inv(st, t, n_partials);
     }
     const u32x4* __restrict__ src = t == 0 ? q : (t == 1 ? k : v);
     u32x2* __restrict__ dst = t == 0 ? q8 : (t == 1 ? k8 : v8);
@@ -217,22 +249,24 @@ hipError_t launch_init_state(DeviceState* st, int history_len, const float stati
 hipError_t launch_quantize_dynamic(DeviceState* st, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                    int64_t n, uint8_t* q8, uint8_t* k8, uint8_t* v8, hipStream_t s) {
     const int64_t chunks = n / 8;
+    // Grid shapes from a sweep at 1 x 8192 tokens, 16 heads (amax: 256
+    // workgroups per tensor, each thread streaming >= 8 chunks; quantize: 16
+    // chunks per thread): 74 % of HBM peak for the pair, against 66 % with
+    // 4x more, thinner workgroups (whose scale prologue then dominates).
     const int ga = grid_for(chunks, 8, kMaxPartials);
-    amax_partial_kernel<<<dim3(ga, 3), kThreads, 0, s>>>((const u32x4*)q, (const u32x4*)k, (const u32x4*)v, chunks,
-                                                         &st->partial[0][0]);
-    finalize_dynamic_kernel<<<1, kFinalizeThreads, 0, s>>>(st, ga);
-    const int gq = grid_for(chunks, 4, 2048);
+    amax_partial_kernel<<<dim3(ga, 3), kThreads, 0, s>>>((const u32x4*)q, (const u32x4*)k, (const u32x4*)v, chunks, st);
+    const int gq = grid_for(chunks, 16, 2048);
     quantize_kernel<false><<<dim3(gq, 3), kThreads, 0, s>>>(st, (const u32x4*)q, (const u32x4*)k, (const u32x4*)v,
-                                                           chunks, (u32x2*)q8, (u32x2*)k8, (u32x2*)v8);
+                                                           chunks, (u32x2*)q8, (u32x2*)k8, (u32x2*)v8, ga);
     return hipGetLastError();
 }
 
 hipError_t launch_quantize_static(DeviceState* st, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                   int64_t n, uint8_t* q8, uint8_t* k8, uint8_t* v8, hipStream_t s) {
     const int64_t chunks = n / 8;
-    const int gq = grid_for(chunks, 4, 2048);
+    const int gq = grid_for(chunks, 16, 2048);
     quantize_kernel<true><<<dim3(gq, 3), kThreads, 0, s>>>(st, (const u32x4*)q, (const u32x4*)k, (const u32x4*)v,
-                                                          chunks, (u32x2*)q8, (u32x2*)k8, (u32x2*)v8);
+                                                          chunks, (u32x2*)q8, (u32x2*)k8, (u32x2*)v8, 1);
     return hipGetLastError();
 }
 
