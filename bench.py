@@ -39,7 +39,71 @@ def parse():
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="instead of the benchmark, time a plain device copy of this many MiB (the known-size "
                         "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
+    p.add_argument("--graph-overhead", action="store_true",
+                   help="instead of the benchmark, compare eager launches with HIP-graph replay of the whole "
+                        "path on the small workloads (1x256 tokens x 2 heads, 1x2304 tokens x 16 heads)")
     return p.parse_args()
+
+
+def graph_overhead(steps):
+    """Per-forward time of the whole path, eager vs replay of a captured HIP graph.
+
+    Small images are where launch overhead matters: the GPU work per forward is a few microseconds, so the
+    eager rate is set by the host's launch path.  Prints one JSON line per (workload, mode)."""
+    import torch
+
+    import quantized_flash_attn_amd as qfa
+    from workloads import WORKLOADS, cu_seqlens_tensor, make_qkv
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    per_graph = 16
+    for wi in (1, 2):
+        w = WORKLOADS[wi]
+        H, T = w.num_heads, w.total_tokens
+        q, k, v = make_qkv(w, 0, device=dev)
+        q8, k8, v8 = (torch.empty((T, H, 128), dtype=torch.uint8, device=dev) for _ in range(3))
+        out = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
+        cu = cu_seqlens_tensor(w.seqlens, dev)
+        for mode in ("dynamic", "static"):
+            st = qfa.init_scale_state(dev, static_amax=[30.0, 30.0, 30.0], margin=1.5)
+            sc = qfa.descale(st)
+
+            def fwd():
+                qfa.quantize_qkv(st, mode, q, k, v, q8, k8, v8)
+                qfa.fp8_varlen_attn(q8, k8, v8, sc, cu, H, out=out)
+
+            def timed(fn, n):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                e0.record(stream)
+                for _ in range(n):
+                    fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                return e0.elapsed_time(e1) * 1e3 / n  # us per call
+
+            for _ in range(20):
+                fwd()
+            eager_us = timed(fwd, steps)
+            g1, g16 = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g1):
+                fwd()
+            with torch.cuda.graph(g16):
+                for _ in range(per_graph):
+                    fwd()
+            for _ in range(5):
+                g1.replay()
+                g16.replay()
+            g1_us = timed(g1.replay, steps)
+            g16_us = timed(g16.replay, max(1, steps // per_graph)) / per_graph
+            print(json.dumps({"graph_overhead": {
+                "workload": w.name, "mode": mode, "steps": steps,
+                "eager_us_per_forward": round(eager_us, 2),
+                "graph_1_forward_us_per_forward": round(g1_us, 2),
+                f"graph_{per_graph}_forwards_us_per_forward": round(g16_us, 2),
+                "attn_flop": w.attn_flop}}), flush=True)
 
 
 def copy_calibration(mib, steps):
@@ -133,6 +197,9 @@ def main():
     args = parse()
     if args.copy_calibration_mib > 0:
         copy_calibration(args.copy_calibration_mib, args.steps)
+        return
+    if args.graph_overhead:
+        graph_overhead(args.steps)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))

@@ -160,6 +160,21 @@ qfa_status qfa_read_scale_state(const qfa_scale_state* st, qfa_scale_snapshot* o
 qfa_status qfa_check_cu_seqlens(const int32_t* cu_seqlens, int num_seqs, int64_t total_tokens,
                                 void* stream);
 
+/*
+ * Calibrate-once export ([P2] Calibrate-Once, Reuse Workflow; [P4] Create
+ * static scales): after dynamic forwards on representative inputs, the scale
+ * each tensor learned, with the save margin applied for a scale file:
+ *   out_amax[t] = fp32(max(ring[t][0..history_len)) * margin),  t = Q, K, V.
+ * The result is an amax-domain value; a state initialised from it with
+ * margin 1.0 reproduces fp32(ring max * margin) exactly.
+ *   margin    finite and > 0 (1.5 is the pages' default save margin)
+ *   out_amax  host float[3] (out); written only on QFA_OK
+ * Synchronises `stream` (reads the device state).  QFA_ERR_STATE if the state
+ * is not initialised or has seen no dynamic forward; QFA_ERR_VALUE if margin
+ * is invalid, a tensor observed only zeros, or a product overflows float32.
+ */
+qfa_status qfa_export_static_amax(const qfa_scale_state* st, float margin, float* out_amax, void* stream);
+
 /* Static text for a status; thread-local detail of the last failure on this thread. */
 const char* qfa_status_string(qfa_status s);
 const char* qfa_last_error(void);

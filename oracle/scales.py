@@ -21,6 +21,10 @@ Readings taken where the pages are silent:
   the maximum, then quantize.
 * A stored static scale is an amax (range) value; the effective amax in
   static mode is ``fp32(static_amax) * fp32(margin)`` and the ring is unused.
+* The scale learned by calibration ("FP8 ViT Encoder Attention",
+  Calibrate-Once, Reuse Workflow; "FP8 vision encoder attention", Create
+  static scales) is the ring maximum after the dynamic forwards, and the
+  saved value is ``fp32(ring max * margin)``; it is loaded with margin 1.0.
 * ``a = max(amax_eff, 2**-100)`` keeps both factors finite for all-zero or
   tiny tensors; ``descale = fp32(a / 448)`` dequantizes and
   ``inv = fp32(448 / a)`` quantizes, each one IEEE float32 division.
@@ -101,6 +105,22 @@ class ScaleState:
         self.amax_eff = self.ring.max(axis=1).astype(np.float32)
         self.descale, self.inv = scales_from_amax(self.amax_eff)
         return self.descale.copy(), self.inv.copy()
+
+    def export_static_amax(self, margin=1.5) -> np.ndarray:
+        """Calibrated amax to save: max over the ring of each tensor times the save margin (float32)."""
+        if self.cursor == 0:
+            raise ValueError("no dynamic forward has been observed")
+        m = np.float32(margin)
+        if not np.isfinite(m) or m <= 0:
+            raise ValueError("margin must be finite and positive")
+        ring_max = self.ring.max(axis=1).astype(np.float32)
+        if np.any(ring_max <= 0):
+            raise ValueError("a tensor observed only zeros")
+        with np.errstate(over="ignore"):
+            out = (ring_max * m).astype(np.float32)
+        if not np.all(np.isfinite(out)):
+            raise ValueError("amax times margin overflows float32")
+        return out
 
     def forward_static(self) -> tuple:
         """Static mode: loaded amax times margin; observed values are ignored."""

@@ -16,6 +16,10 @@ Entry points (same names as the C ABI without the ``qfa_`` prefix):
 * ``fp8_varlen_attn(q8, k8, v8, scales, cu_seqlens, num_heads, head_dim=128, out=None)``
 * ``read_scale_state(state)`` -> dict (synchronises; for tests and checkpoints)
 * ``check_cu_seqlens(cu_seqlens, total_tokens)`` (synchronises)
+* ``export_static_amax(state, margin=1.5)`` -> ``[q, k, v]`` (synchronises)
+
+Scale files (calibrate once, load as static scales) are read and written by
+``quantized_flash_attn_amd.scale_file``.
 """
 
 import ctypes
@@ -81,7 +85,7 @@ class _Snapshot(ctypes.Structure):
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(
-            f"{_LIB_PATH} is missing: build it with `python -m quantized_flash_attn_amd.build` "
+            f"{_LIB_PATH} is missing: build it with `python quantized_flash_attn_amd/build.py` "
             "(there is no non-HIP fallback)"
         )
     lib = ctypes.CDLL(_LIB_PATH)
@@ -94,6 +98,7 @@ def _load():
         "qfa_fp8_varlen_attn": (i32, [vp, vp, vp, vp, vp, i32, i64, i32, i32, vp, vp]),
         "qfa_read_scale_state": (i32, [ctypes.POINTER(_State), ctypes.POINTER(_Snapshot), vp]),
         "qfa_check_cu_seqlens": (i32, [vp, i32, i64, vp]),
+        "qfa_export_static_amax": (i32, [ctypes.POINTER(_State), f32, ctypes.POINTER(ctypes.c_float), vp]),
         "qfa_status_string": (ctypes.c_char_p, [i32]),
         "qfa_last_error": (ctypes.c_char_p, []),
     }
@@ -115,6 +120,7 @@ EXPORTS = (
     "qfa_fp8_varlen_attn",
     "qfa_read_scale_state",
     "qfa_check_cu_seqlens",
+    "qfa_export_static_amax",
     "qfa_status_string",
     "qfa_last_error",
 )
@@ -273,3 +279,11 @@ def check_cu_seqlens(cu_seqlens, total_tokens: int):
     with torch.cuda.device(cu_seqlens.device):
         _check(_lib.qfa_check_cu_seqlens(cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, int(total_tokens),
                                          _stream_ptr(cu_seqlens.device)))
+
+
+def export_static_amax(state: ScaleState, margin: float = 1.5) -> list:
+    """Calibrated static amax of Q, K, V: fp32(ring maximum * margin) (synchronises)."""
+    out = (ctypes.c_float * 3)()
+    with torch.cuda.device(state.buffer.device):
+        _check(_lib.qfa_export_static_amax(state.handle, ctypes.c_float(margin), out, _stream_ptr(state.buffer.device)))
+    return [float(x) for x in out]

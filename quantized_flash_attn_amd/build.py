@@ -1,6 +1,8 @@
 """Compile the HIP sources into quantized_flash_attn_amd/libqfa.so (gfx950 only).
 
-Run ``python -m quantized_flash_attn_amd.build`` (or ``__graft_entry__.build()``).
+Run ``python quantized_flash_attn_amd/build.py`` (or ``__graft_entry__.build()``).
+Run it as a script, not as ``-m quantized_flash_attn_amd.build``: importing the
+package loads the library, which is missing before the first build.
 hipcc cross-compiles for gfx950 without a GPU present.
 """
 

@@ -184,6 +184,30 @@ qfa_status qfa_read_scale_state(const qfa_scale_state* st, qfa_scale_snapshot* o
     return ok();
 }
 
+qfa_status qfa_export_static_amax(const qfa_scale_state* st, float margin, float* out_amax, void* stream) {
+    const char* where = "qfa_export_static_amax";
+    if (!st || !out_amax) return fail(QFA_ERR_NULL, "%s: null pointer", where);
+    if (st->magic != QFA_STATE_MAGIC || !st->device) return fail(QFA_ERR_STATE, "%s: state not initialised", where);
+    if (!std::isfinite(margin) || !(margin > 0.0f)) return fail(QFA_ERR_VALUE, "%s: margin must be finite and positive", where);
+    qfa::DeviceState h;
+    hipError_t e = hipMemcpyAsync(&h, st->device, offsetof(qfa::DeviceState, partial), hipMemcpyDeviceToHost,
+                                  (hipStream_t)stream);
+    if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return check_launch(e, where);
+    if (h.cursor <= 0) return fail(QFA_ERR_STATE, "%s: no dynamic forward has been observed", where);
+    float res[3];
+    for (int t = 0; t < 3; ++t) {
+        float m = 0.0f;  // unfilled slots hold 0; amax values are never negative
+        for (int j = 0; j < h.history_len; ++j) m = h.ring[t][j] > m ? h.ring[t][j] : m;
+        if (!(m > 0.0f)) return fail(QFA_ERR_VALUE, "%s: tensor %d observed only zeros", where, t);
+        volatile float prod = m * margin;  // one float32 multiply
+        res[t] = prod;
+        if (!std::isfinite(res[t])) return fail(QFA_ERR_VALUE, "%s: amax[%d] * margin overflows float32", where, t);
+    }
+    for (int t = 0; t < 3; ++t) out_amax[t] = res[t];
+    return ok();
+}
+
 qfa_status qfa_check_cu_seqlens(const int32_t* cu_seqlens, int num_seqs, int64_t total_tokens, void* stream) {
     const char* where = "qfa_check_cu_seqlens";
     if (!cu_seqlens) return fail(QFA_ERR_NULL, "%s: null cu_seqlens", where);

@@ -30,7 +30,7 @@ def header_functions():
 
 def test_header_symbols_exported():
     declared = header_functions()
-    assert len(declared) == 9, declared
+    assert len(declared) == 10, declared
     out = subprocess.run(["nm", "-D", "--defined-only", qfa.library_path()], stdout=subprocess.PIPE, text=True).stdout
     exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
     missing = [f for f in declared if f not in exported]
@@ -129,6 +129,12 @@ def test_other_entry_points_validation():
     assert lib.qfa_check_cu_seqlens(None, 1, 8, None) == NULL
     assert lib.qfa_check_cu_seqlens(FAKE, 0, 8, None) == SHAPE
     assert lib.qfa_check_cu_seqlens(FAKE, 1, -1, None) == SHAPE
+    out = (ctypes.c_float * 3)()
+    assert lib.qfa_export_static_amax(None, 1.5, out, None) == NULL
+    assert lib.qfa_export_static_amax(ctypes.byref(_handle()), 1.5, None, None) == NULL
+    assert lib.qfa_export_static_amax(ctypes.byref(_handle(magic=0)), 1.5, out, None) == STATE
+    for m in (0.0, -1.5, float("inf"), float("nan")):
+        assert lib.qfa_export_static_amax(ctypes.byref(_handle()), m, out, None) == VALUE
 
 
 def test_binding_refuses_cpu_tensors():

@@ -169,3 +169,57 @@ def test_scale_file_example_from_page():
                 assert d[t] == np.float32(exp["descale"])
             if "inv" in exp:
                 assert i[t] == np.float32(exp["inv"])
+
+
+def test_export_is_max_of_last_window_times_margin():
+    """Calibration export = max of the last history_len observations x margin, one float32 multiply.
+
+    Brute force over the list of observations (not the ring): checks the slot
+    arithmetic of the ring, the wrap after history_len forwards and the single
+    rounding of the margin product.
+    """
+    rng = np.random.default_rng(77)
+    for hist in (16, 3, 1):
+        st = ScaleState(history_len=hist)
+        seen = [[], [], []]
+        for n in range(1, 41):
+            obs = (rng.uniform(0.5, 2.0, 3) * 2.0 ** rng.integers(-20, 20, 3)).astype(np.float32)
+            st.forward_dynamic(obs)
+            for t in range(3):
+                seen[t].append(obs[t])
+            for margin in (1.5, 1.0, 1.1):
+                got = st.export_static_amax(margin)
+                for t in range(3):
+                    window = seen[t][max(0, n - hist):n]
+                    want = round_fraction_to_f32(Fraction(float(max(window))) * Fraction(float(np.float32(margin))))
+                    assert got[t] == want, (hist, n, t, margin)
+
+
+def test_export_refusals():
+    with pytest.raises(ValueError):
+        ScaleState().export_static_amax(1.5)                 # nothing observed yet
+    st = ScaleState()
+    st.forward_dynamic([1.0, 0.0, 1.0])
+    with pytest.raises(ValueError):
+        st.export_static_amax(1.5)                           # V observed only zeros
+    st = ScaleState()
+    st.forward_dynamic([3e38, 1.0, 1.0])
+    with pytest.raises(ValueError):
+        st.export_static_amax(1.5)                           # product overflows float32
+    for m in (0.0, -1.0, float("nan")):
+        with pytest.raises(ValueError):
+            st.export_static_amax(m)
+
+
+def test_export_then_load_equals_margin_at_load():
+    """fp32(fp32(a * m) * 1) == fp32(a * m): saving with the margin and loading with margin 1.0
+    gives the same scales as loading the raw ring maximum with the margin."""
+    st = ScaleState()
+    for obs in ([224.3, 0.7, 13.0], [100.0, 1.9, 12.5], [3.3, 0.2, 99.0]):
+        st.forward_dynamic(np.array(obs, np.float32))
+    saved = st.export_static_amax(1.5)
+    a = ScaleState(static_amax=saved, margin=1.0)
+    b = ScaleState(static_amax=st.ring.max(axis=1), margin=1.5)
+    da, ia = a.forward_static()
+    db, ib = b.forward_static()
+    assert np.array_equal(da, db) and np.array_equal(ia, ib)
