@@ -10,7 +10,9 @@ step's bf16 reads come from HBM.
 
 Prints ONE JSON line.  Work convention: 4 * sum(n_b^2) * H * 128 flop
 (two matmuls, 2 flop per multiply-add; softmax and the lo-term MFMAs not
-counted).  Peaks: dense FP8 MFMA 5000 TFLOP/s, HBM 8000 GB/s.
+counted).  Peaks: dense FP8 MFMA 5000 TFLOP/s, dense BF16 MFMA 2500 TFLOP/s,
+HBM 8000 GB/s.  Besides the step, it times attention alone, the quantize path
+alone, and the BF16 attention baseline on the same bf16 inputs.
 """
 
 import argparse
@@ -23,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 FP8_PEAK_TFLOPS = 5000.0
+BF16_PEAK_TFLOPS = 2500.0
 HBM_PEAK_GBS = 8000.0
 METRIC = "FP8 varlen ViT attn TFLOP/s incl. QKV quant (seq 8192, d=128), % fp8 peak"
 
@@ -250,6 +253,8 @@ def main():
     # component timings on the same stream
     ms_attn = timed(lambda i: qfa.fp8_varlen_attn(q8, k8, v8, scales, cu, H, out=out), args.steps)
     ms_quant = timed(lambda i: qfa.quantize_qkv(st, "dynamic", *sets[i % len(sets)], q8, k8, v8), args.steps)
+    # the BF16 baseline on the same inputs (the pages state FP8 gains as BF16 -> FP8 pairs)
+    ms_bf16 = timed(lambda i: qfa.bf16_varlen_attn(*sets[i % len(sets)], cu, H, out=out), args.steps)
 
     flop = w.attn_flop
     value = flop / (ms_step * 1e-3) / 1e12
@@ -275,6 +280,10 @@ def main():
         "frac_fp8_peak_incl_quant": round(value / FP8_PEAK_TFLOPS, 4),
         "attention": {"ms": round(ms_attn, 4), "tflops": round(attn_tflops, 1),
                       "frac_fp8_peak": round(attn_tflops / FP8_PEAK_TFLOPS, 4)},
+        "bf16_attention": {"ms": round(ms_bf16, 4), "tflops": round(flop / (ms_bf16 * 1e-3) / 1e12, 1),
+                           "frac_bf16_peak": round(flop / (ms_bf16 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                           "fp8_speedup_incl_quant": round(ms_bf16 / ms_step, 3),
+                           "fp8_speedup_attention_only": round(ms_bf16 / ms_attn, 3)},
         "quantize_dynamic": {"ms": round(ms_quant, 4), "algorithmic_bytes": quant_bytes, "gbs": round(quant_gbs, 1),
                              "frac_hbm_peak": round(quant_gbs / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",

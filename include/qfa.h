@@ -151,6 +151,23 @@ qfa_status qfa_fp8_varlen_attn(const uint8_t* q8, const uint8_t* k8, const uint8
                                void* stream);
 
 /*
+ * Varlen BF16 attention, the baseline FP8 attention is compared against
+ * ([P2] Performance and [P4] Expected performance give every FP8 result as
+ * a BF16 -> FP8 pair on the same shapes).
+ *   out[i,h,:] = sum_j softmax_j(<q_i,k_j>/sqrt(128)) * v_j
+ * over the keys j of the sequence that contains token i, non-causal.
+ *   q, k, v        device bf16 [total_tokens, num_heads, 128]
+ *   cu_seqlens     device int32[num_seqs + 1], same rules as qfa_fp8_varlen_attn
+ *   out            device bf16 [total_tokens, num_heads, 128] (out)
+ * total_tokens must be below 2^31.  Products and sums run in fp32 on bf16
+ * MFMA operands; the probabilities are rounded to bf16 for the P*V product.
+ * Same status codes as qfa_fp8_varlen_attn.
+ */
+qfa_status qfa_bf16_varlen_attn(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                                int num_seqs, int64_t total_tokens, int num_heads, int head_dim, void* out,
+                                void* stream);
+
+/*
  * Debug/checkpoint helpers (synchronise `stream`; not for the hot path).
  * qfa_read_scale_state copies the device state to *out.
  * qfa_check_cu_seqlens reads cu_seqlens back and returns QFA_ERR_DATA unless

@@ -25,7 +25,9 @@ section):
 * ``attention``-- softmax attention over packed variable-length sequences with
                   per-tensor scales ("FP8 vision encoder attention",
                   Requirements: packed variable-length batches, a per-tensor
-                  FP8 varlen attention function), in float64.
+                  FP8 varlen attention function), in float64; the same
+                  definition on bf16 inputs for the BF16 baseline ("FP8 ViT
+                  Encoder Attention", Performance).
 
 Pins: every function here is checked by ``tests/test_oracle_*.py`` against
 something other than itself (the OCP format table, torch-CPU's float8 cast,
@@ -43,7 +45,7 @@ from .scales import (
     static_amax_eff,
 )
 from .quantize import quantize, quantize_qkv
-from .attention import attention, attention_rows
+from .attention import attention, attention_float, attention_float_rows, attention_rows
 
 __all__ = [
     "DECODE_TABLE",
@@ -60,4 +62,6 @@ __all__ = [
     "quantize_qkv",
     "attention",
     "attention_rows",
+    "attention_float",
+    "attention_float_rows",
 ]

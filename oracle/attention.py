@@ -12,6 +12,11 @@ The oracle dequantizes the same E4M3 codes the GPU consumes
 (``decode(code) * scale`` in float64) and evaluates the plain definition in
 float64: ``S = Q K^T / sqrt(D)``, a row softmax with its maximum subtracted,
 ``O = P V``.
+
+``attention_float`` / ``attention_float_rows`` evaluate the same definition
+on real-valued inputs (the bf16 Q, K, V of the BF16 baseline that "FP8 ViT
+Encoder Attention", Performance, and "FP8 vision encoder attention",
+Expected performance, compare FP8 against).
 """
 
 import math
@@ -36,6 +41,51 @@ def _softmax_rows(s):
     s = s - s.max(axis=-1, keepdims=True)
     p = np.exp(s)
     return p / p.sum(axis=-1, keepdims=True)
+
+
+def _attend(qf, kf, vf, magnitude):
+    """One sequence and head, float64: (P V, P |V| or None)."""
+    p = _softmax_rows(qf @ kf.T * (1.0 / math.sqrt(qf.shape[-1])))
+    return p @ vf, (p @ np.abs(vf) if magnitude else None)
+
+
+def attention_float(q, k, v, cu_seqlens, magnitude=False):
+    """Full output, float64 ``[T, H, D]``, from real-valued ``[T, H, D]`` inputs (e.g. bf16 values)."""
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    T, H, D = q.shape
+    cu = _check_cu(cu_seqlens, T)
+    out = np.zeros((T, H, D), dtype=np.float64)
+    mag = np.zeros((T, H, D), dtype=np.float64) if magnitude else None
+    for b in range(cu.size - 1):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        for h in range(H):
+            if hi == lo:
+                continue
+            o, m = _attend(q[lo:hi, h], k[lo:hi, h], v[lo:hi, h], magnitude)
+            out[lo:hi, h] = o
+            if magnitude:
+                mag[lo:hi, h] = m
+    return (out, mag) if magnitude else out
+
+
+def attention_float_rows(q, k, v, cu_seqlens, rows, magnitude=False):
+    """Output rows ``rows`` (global token indices) of ``attention_float`` only."""
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    T, H, D = q.shape
+    cu = _check_cu(cu_seqlens, T)
+    rows = np.asarray(rows, dtype=np.int64)
+    seq_of = np.searchsorted(cu, rows, side="right") - 1
+    out = np.zeros((rows.size, H, D), dtype=np.float64)
+    mag = np.zeros((rows.size, H, D), dtype=np.float64) if magnitude else None
+    for b in np.unique(seq_of):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        sel = np.nonzero(seq_of == b)[0]
+        for h in range(H):
+            o, m = _attend(q[rows[sel], h], k[lo:hi, h], v[lo:hi, h], magnitude)
+            out[sel, h] = o
+            if magnitude:
+                mag[sel, h] = m
+    return (out, mag) if magnitude else out
 
 
 def attention(q8, k8, v8, descale, cu_seqlens, magnitude=False):

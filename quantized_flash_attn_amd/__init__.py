@@ -14,6 +14,7 @@ Entry points (same names as the C ABI without the ``qfa_`` prefix):
 * ``quantize_qkv(state, mode, q, k, v, q8=None, k8=None, v8=None)`` -> ``(q8, k8, v8)``
 * ``descale(state)`` -> device float32[3] view {s_q, s_k, s_v}
 * ``fp8_varlen_attn(q8, k8, v8, scales, cu_seqlens, num_heads, head_dim=128, out=None)``
+* ``bf16_varlen_attn(q, k, v, cu_seqlens, num_heads, head_dim=128, out=None)`` (the BF16 baseline)
 * ``read_scale_state(state)`` -> dict (synchronises; for tests and checkpoints)
 * ``check_cu_seqlens(cu_seqlens, total_tokens)`` (synchronises)
 * ``export_static_amax(state, margin=1.5)`` -> ``[q, k, v]`` (synchronises)
@@ -96,6 +97,7 @@ def _load():
         "qfa_quantize_qkv": (i32, [ctypes.POINTER(_State), i32, vp, vp, vp, i64, i32, i32, vp, vp, vp, vp]),
         "qfa_descale_ptr": (vp, [ctypes.POINTER(_State)]),
         "qfa_fp8_varlen_attn": (i32, [vp, vp, vp, vp, vp, i32, i64, i32, i32, vp, vp]),
+        "qfa_bf16_varlen_attn": (i32, [vp, vp, vp, vp, i32, i64, i32, i32, vp, vp]),
         "qfa_read_scale_state": (i32, [ctypes.POINTER(_State), ctypes.POINTER(_Snapshot), vp]),
         "qfa_check_cu_seqlens": (i32, [vp, i32, i64, vp]),
         "qfa_export_static_amax": (i32, [ctypes.POINTER(_State), f32, ctypes.POINTER(ctypes.c_float), vp]),
@@ -118,6 +120,7 @@ EXPORTS = (
     "qfa_quantize_qkv",
     "qfa_descale_ptr",
     "qfa_fp8_varlen_attn",
+    "qfa_bf16_varlen_attn",
     "qfa_read_scale_state",
     "qfa_check_cu_seqlens",
     "qfa_export_static_amax",
@@ -253,6 +256,28 @@ def fp8_varlen_attn(q8, k8, v8, scales, cu_seqlens, num_heads=None, head_dim=HEA
         _check(_lib.qfa_fp8_varlen_attn(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), scales.data_ptr(),
                                         cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, T, H, head_dim,
                                         out.data_ptr(), _stream_ptr(q8.device)))
+    return out
+
+
+def bf16_varlen_attn(q, k, v, cu_seqlens, num_heads=None, head_dim=HEAD_DIM, out=None):
+    """bf16 attention output ``[T, H, 128]`` from bf16 Q, K, V (the BF16 baseline of the FP8 path)."""
+    _require_gpu(q, k, v, cu_seqlens)
+    T, H, D = _qkv_shape(q)
+    if num_heads is not None and num_heads != H:
+        raise ValueError("num_heads does not match q")
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16 or tuple(t.shape) != (T, H, D) or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous bf16 tensors of one shape")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be int32[num_seqs + 1]")
+    if out is None:
+        out = torch.empty((T, H, D), dtype=torch.bfloat16, device=q.device)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (T, H, D) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 tensor of the input shape")
+    with torch.cuda.device(q.device):
+        _check(_lib.qfa_bf16_varlen_attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(),
+                                         cu_seqlens.numel() - 1, T, H, head_dim, out.data_ptr(),
+                                         _stream_ptr(q.device)))
     return out
 
 

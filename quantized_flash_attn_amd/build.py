@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libqfa.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["abi.hip", "quant.hip", "attn.hip"]
+SOURCES = ["abi.hip", "quant.hip", "attn.hip", "attn_bf16.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -165,6 +165,27 @@ qfa_status qfa_fp8_varlen_attn(const uint8_t* q8, const uint8_t* k8, const uint8
     return check_launch(e, where);
 }
 
+qfa_status qfa_bf16_varlen_attn(const void* q, const void* k, const void* v, const int32_t* cu_seqlens, int num_seqs,
+                                int64_t total_tokens, int num_heads, int head_dim, void* out, void* stream) {
+    const char* where = "qfa_bf16_varlen_attn";
+    int64_t n = 0;
+    qfa_status s = check_shape(total_tokens, num_heads, head_dim, &n, where);
+    if (s != QFA_OK) return s;
+    if (num_seqs < 1) return fail(QFA_ERR_SHAPE, "%s: num_seqs %d must be at least 1", where, num_seqs);
+    if (total_tokens >= (INT64_C(1) << 31)) return fail(QFA_ERR_SHAPE, "%s: total_tokens must be below 2^31", where);
+    if (!cu_seqlens) return fail(QFA_ERR_NULL, "%s: null cu_seqlens", where);
+    if (n > 0 && (!q || !k || !v || !out)) return fail(QFA_ERR_NULL, "%s: null tensor pointer", where);
+    if (n > 0 && !(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out)))
+        return fail(QFA_ERR_ALIGN, "%s: tensor pointer not 16-byte aligned", where);
+    if ((uintptr_t)cu_seqlens & 3u) return fail(QFA_ERR_ALIGN, "%s: cu_seqlens not 4-byte aligned", where);
+    s = check_pending(where);
+    if (s != QFA_OK) return s;
+    if (n == 0) return ok();
+    const hipError_t e = qfa::launch_attention_bf16(q, k, v, cu_seqlens, num_seqs, (int)total_tokens, num_heads, out,
+                                                    (hipStream_t)stream);
+    return check_launch(e, where);
+}
+
 qfa_status qfa_read_scale_state(const qfa_scale_state* st, qfa_scale_snapshot* out, void* stream) {
     const char* where = "qfa_read_scale_state";
     if (!st || !out) return fail(QFA_ERR_NULL, "%s: null pointer", where);

@@ -50,33 +50,14 @@
 //                   l sums the unquantized p in fp32.
 //   epilogue        out = bf16(O * s_v / l).
 
-#include "qfa_internal.h"
+#include "attn_common.h"
 
 namespace qfa {
 namespace {
 
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-typedef int v2i __attribute__((ext_vector_type(2)));
-typedef float v2f __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) unsigned char lds_u8;
+using namespace attn;
 
-constexpr int kD = 128;             // head_dim
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kGroupThreads = kThreads / 2;
-constexpr int kQB = 2;              // 16-query MFMA blocks per wave
-constexpr int kBM = kWaves * kQB * 16;  // 256 queries per workgroup
-constexpr int kBN = 128;            // keys per tile
 constexpr int kKRow = 2 * kD + 16;  // bytes per bf16 K row in LDS (256 + 16 B of padding)
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRsqrtD = 0.08838834764831845f;  // 1/sqrt(128)
-constexpr float kRescaleSlack = 0.5f;            // log2 units the running max may lag
-constexpr float kMInit = -1e30f;                 // finite "no max yet", so c = 0 gives no NaN
 
 // LDS map (bytes): two fp8 K staging buffers | two bf16 K buffers | two fp8
 // V buffers = 132 KiB.
@@ -93,9 +74,6 @@ static_assert(kLdsV % 128 == 0 && kVBuf % 128 == 0, "V buffers must keep address
 __device__ inline v4f mfma_f8(v8i a, v8i b, v4f c) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
-__device__ inline v4f mfma_bf16(bf16x8 a, bf16x8 b, v4f c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
 
 // Four E4M3 codes (one dword) -> four bf16 values, exactly (scale 1).
 __device__ inline bf16x4 codes_to_bf16(uint32_t w) {
@@ -106,22 +84,6 @@ __device__ inline bf16x4 codes_to_bf16(uint32_t w) {
 __device__ inline bf16x8 codes_to_bf16x8(uint32_t w0, uint32_t w1) {
     const bf16x4 a = codes_to_bf16(w0), b = codes_to_bf16(w1);
     return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-
-// Maximum over the four lanes {l, l^16, l^32, l^48} that hold one query.
-__device__ inline float quad_max(float x) {
-    const v2i a = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
-    x = fmaxf(__int_as_float(a[0]), __int_as_float(a[1]));
-    const v2i b = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
-    return fmaxf(__int_as_float(b[0]), __int_as_float(b[1]));
-}
-
-// Sum over the four lanes that hold one query.
-__device__ inline float quad_sum(float x) {
-    const v2i a = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
-    x = __int_as_float(a[0]) + __int_as_float(a[1]);
-    const v2i b = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
-    return __int_as_float(b[0]) + __int_as_float(b[1]);
 }
 
 // LDS layouts:
@@ -135,9 +97,6 @@ __device__ inline float quad_sum(float x) {
 //      swz_v(r) = (r & 3) | ((r >> 4) & 1) << 2.
 //   fp8 K staging: unswizzled [key][128].
 __device__ inline uint32_t swz_v(uint32_t row) { return (row & 3) | ((row >> 2) & 4); }
-
-// Buffer descriptor word 3 for raw byte addressing on gfx9-family GPUs.
-constexpr int kRsrcWord3 = 0x00020000;
 
 // Asynchronous fetch of one 128-key tile of K (fp8 staging) or V: wave w
 // fills the 1 KiB segments 2w and 2w + 1 (tile rows [16w, 16w + 16)); lane
@@ -158,31 +117,6 @@ __device__ inline void issue_tile_load(const uint8_t* __restrict__ src, uint32_t
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)(src + off), 0, nrec, kRsrcWord3);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + seg * 1024, 16, (int)lane_off, 0, 0, 0);
     }
-}
-
-__device__ inline void wait_async_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Tile id -> (sequence, query tile).  Sequence b owns the virtual tiles
-// [floor(cu[b]/BM) + b, floor(cu[b+1]/BM) + b + 1): enough for its
-// ceil(n_b/BM) tiles, at most one spare.  Virtual tiles per head:
-// floor(T/BM) + B.  The start positions increase strictly with b, so a
-// binary search over cu_seqlens finds the owner.
-__device__ inline int find_sequence(const int32_t* __restrict__ cu, int num_seqs, int vt) {
-    int lo = 0, hi = num_seqs - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        const int start = cu[mid] / kBM + mid;
-        if (start <= vt) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-}
-
-// Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
-// contiguous range of logical tiles so tiles sharing K/V share an L2.
-__device__ inline int xcd_remap(int bid, int nwg) {
-    const int q = nwg / 8, r = nwg % 8;
-    const int x = bid % 8, k = bid / 8;
-    return x * q + min(x, r) + k;
 }
 
 // Everything one wave carries through the key loop.  Lane (r16, g) of a
@@ -258,65 +192,6 @@ __device__ __forceinline__ void qk_phase(const Wave& w, const unsigned char* sme
 #pragma unroll
             for (int qb = 0; qb < kQB; ++qb) s[kb][qb] = mfma_bf16(kop, w.q[qb][c], s[kb][qb]);
         }
-    }
-}
-
-// Scores -> probabilities p = 2^(S c + 8 - m c) for one key tile with nk
-// valid keys.  If the tile's row max exceeds m by more than the slack
-// anywhere in the wave, m moves to it for every query and O and l (which
-// hold the earlier tiles) are rescaled.
-__device__ __forceinline__ void exp_phase(Wave& w, v4f (&s)[8][kQB], int nk) {
-    if (nk < kBN) {
-#pragma unroll
-        for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool dead = w.g4 >= nk - 16 * kb - i;
-#pragma unroll
-                for (int qb = 0; qb < kQB; ++qb) s[kb][qb][i] = dead ? -INFINITY : s[kb][qb][i];
-            }
-    }
-    float mn[kQB];
-    bool grow = false;
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-        float mx = s[0][qb][0];
-#pragma unroll
-        for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][qb][i]);
-        mn[qb] = fmaxf(w.m[qb], quad_max(mx));
-        grow |= (mn[qb] - w.m[qb]) * w.cexp > kRescaleSlack;
-    }
-    if (__any(grow)) {
-#pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) {
-            const float alpha = __builtin_amdgcn_exp2f((w.m[qb] - mn[qb]) * w.cexp);
-            w.m[qb] = mn[qb];
-            w.l[qb] *= alpha;
-#pragma unroll
-            for (int db = 0; db < 8; ++db) w.o[db][qb] *= alpha;
-        }
-    }
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-        const float bias = 8.0f - w.m[qb] * w.cexp;
-#pragma unroll
-        for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                s[kb][qb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][i], w.cexp, bias));
-    }
-    if (nk < kBN) {
-        // p of masked keys is exactly 0 (also where c = 0 made -inf * c a NaN)
-#pragma unroll
-        for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool dead = w.g4 >= nk - 16 * kb - i;
-#pragma unroll
-                for (int qb = 0; qb < kQB; ++qb) s[kb][qb][i] = dead ? 0.0f : s[kb][qb][i];
-            }
     }
 }
 
@@ -547,12 +422,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
 hipError_t launch_attention(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* scales,
                             const int32_t* cu_seqlens, int num_seqs, int total_tokens, int num_heads, void* out,
                             hipStream_t s) {
-    const int tiles_per_head = total_tokens / kBM + num_seqs;
-    const long long nwg = (long long)tiles_per_head * num_heads;
+    const int tph = tiles_per_head(total_tokens, num_seqs);
+    const long long nwg = (long long)tph * num_heads;
     if (nwg <= 0) return hipSuccess;
     if (nwg > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
     attn_fwd_kernel<<<(unsigned)nwg, kThreads, 0, s>>>(q8, k8, v8, scales, cu_seqlens, num_seqs, num_heads,
-                                                       tiles_per_head, (__bf16*)out);
+                                                       tph, (__bf16*)out);
     return hipGetLastError();
 }
 

@@ -1,0 +1,151 @@
+// Pieces shared by the two varlen attention kernels (E4M3 inputs in attn.hip,
+// bf16 inputs in attn_bf16.hip): the workgroup shape, the tile -> sequence
+// mapping, the XCD-aware workgroup order, the asynchronous tile loads, and
+// the online-softmax step.  Both kernels compute non-causal softmax
+// attention over packed variable-length sequences ("FP8 vision encoder
+// attention", Requirements): each query attends to every key of its own
+// sequence [cu[b], cu[b+1]).
+#pragma once
+
+#include "qfa_internal.h"
+
+namespace qfa {
+namespace attn {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+constexpr int kD = 128;             // head_dim
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kGroupThreads = kThreads / 2;
+constexpr int kQB = 2;              // 16-query MFMA blocks per wave
+constexpr int kBM = kWaves * kQB * 16;  // 256 queries per workgroup
+constexpr int kBN = 128;            // keys per tile
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRsqrtD = 0.08838834764831845f;  // 1/sqrt(128)
+constexpr float kRescaleSlack = 0.5f;            // log2 units the running max may lag
+constexpr float kMInit = -1e30f;                 // finite "no max yet", so c = 0 gives no NaN
+
+// Buffer descriptor word 3 for raw byte addressing on gfx9-family GPUs.
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ inline v4f mfma_bf16(bf16x8 a, bf16x8 b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Maximum over the four lanes {l, l^16, l^32, l^48} that hold one query.
+__device__ inline float quad_max(float x) {
+    const v2i a = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+    x = fmaxf(__int_as_float(a[0]), __int_as_float(a[1]));
+    const v2i b = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+    return fmaxf(__int_as_float(b[0]), __int_as_float(b[1]));
+}
+
+// Sum over the four lanes that hold one query.
+__device__ inline float quad_sum(float x) {
+    const v2i a = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+    x = __int_as_float(a[0]) + __int_as_float(a[1]);
+    const v2i b = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+    return __int_as_float(b[0]) + __int_as_float(b[1]);
+}
+
+__device__ inline void wait_async_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Tile id -> (sequence, query tile).  Sequence b owns the virtual tiles
+// [floor(cu[b]/BM) + b, floor(cu[b+1]/BM) + b + 1): enough for its
+// ceil(n_b/BM) tiles, at most one spare.  Virtual tiles per head:
+// floor(T/BM) + B.  The start positions increase strictly with b, so a
+// binary search over cu_seqlens finds the owner.
+__device__ inline int find_sequence(const int32_t* __restrict__ cu, int num_seqs, int vt) {
+    int lo = 0, hi = num_seqs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        const int start = cu[mid] / kBM + mid;
+        if (start <= vt) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Virtual query tiles per head for the mapping above.
+inline int tiles_per_head(int total_tokens, int num_seqs) { return total_tokens / kBM + num_seqs; }
+
+// Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
+// contiguous range of logical tiles so tiles sharing K/V share an L2.
+__device__ inline int xcd_remap(int bid, int nwg) {
+    const int q = nwg / 8, r = nwg % 8;
+    const int x = bid % 8, k = bid / 8;
+    return x * q + min(x, r) + k;
+}
+
+// Scores -> probabilities p = 2^(S c + 8 - m c) for one key tile with nk
+// valid keys.  s[kb][qb] holds keys 16kb + 4g + i of query r16 (lane
+// (r16, g), g4 = 4g).  If the tile's row max exceeds m by more than the
+// slack anywhere in the wave, m moves to it for every query and O and l
+// (which hold the earlier tiles) are rescaled.  W carries m[kQB], l[kQB],
+// o[8][kQB], cexp and g4.
+template <class W>
+__device__ __forceinline__ void exp_phase(W& w, v4f (&s)[8][kQB], int nk) {
+    if (nk < kBN) {
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool dead = w.g4 >= nk - 16 * kb - i;
+#pragma unroll
+                for (int qb = 0; qb < kQB; ++qb) s[kb][qb][i] = dead ? -INFINITY : s[kb][qb][i];
+            }
+    }
+    float mn[kQB];
+    bool grow = false;
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+        float mx = s[0][qb][0];
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][qb][i]);
+        mn[qb] = fmaxf(w.m[qb], quad_max(mx));
+        grow |= (mn[qb] - w.m[qb]) * w.cexp > kRescaleSlack;
+    }
+    if (__any(grow)) {
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) {
+            const float alpha = __builtin_amdgcn_exp2f((w.m[qb] - mn[qb]) * w.cexp);
+            w.m[qb] = mn[qb];
+            w.l[qb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < 8; ++db) w.o[db][qb] *= alpha;
+        }
+    }
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+        const float bias = 8.0f - w.m[qb] * w.cexp;
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                s[kb][qb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][i], w.cexp, bias));
+    }
+    if (nk < kBN) {
+        // p of masked keys is exactly 0 (also where c = 0 made -inf * c a NaN)
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool dead = w.g4 >= nk - 16 * kb - i;
+#pragma unroll
+                for (int qb = 0; qb < kQB; ++qb) s[kb][qb][i] = dead ? 0.0f : s[kb][qb][i];
+            }
+    }
+}
+
+}  // namespace attn
+}  // namespace qfa

@@ -38,5 +38,7 @@ hipError_t launch_quantize_static(DeviceState* st, const uint16_t* q, const uint
 hipError_t launch_attention(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* scales,
                             const int32_t* cu_seqlens, int num_seqs, int total_tokens, int num_heads,
                             void* out, hipStream_t s);
+hipError_t launch_attention_bf16(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                                 int num_seqs, int total_tokens, int num_heads, void* out, hipStream_t s);
 
 }  // namespace qfa

@@ -16,6 +16,16 @@ import torch
 TOL_MAX = 3e-2
 TOL_MEAN = 3e-3
 
+# BF16 baseline attention (bf16 inputs, fp32 products and sums, P rounded to
+# bf16, bf16 output).  With e as above and M = P|V|: rounding P to bf16 moves
+# the numerator by at most 2^-8 M / l relative to the fp32 denominator
+# (nearest-even rounding, 8 significant bits), and the bf16 output adds at
+# most 2^-8 |r| <= 2^-8 M; the fp32 products, sums and exp2 add terms near
+# 2^-20.  So e <= 2^-7 ~= 7.8e-3 everywhere; the mean of independent
+# roundings is far smaller.
+TOL_MAX_BF16 = 1e-2
+TOL_MEAN_BF16 = 2e-3
+
 
 def log(msg):
     print(msg, flush=True)
@@ -40,7 +50,27 @@ def attn_errors(g: np.ndarray, r: np.ndarray, scale=None):
     return float(e.max()), float(e.mean())
 
 
-def assert_attn_close(g, r, what="", mag=None):
+def sample_rows(w):
+    """Rows checked at full size: all rows, or seeded samples of the workload's ranges."""
+    if not w.oracle_rows:
+        if w.total_tokens <= 2304:
+            return np.arange(w.total_tokens)
+        step = max(1, w.total_tokens // 1024)
+        return np.unique(np.concatenate([np.arange(0, w.total_tokens, step),
+                                         np.arange(w.total_tokens - 128, w.total_tokens)]))
+    rng = np.random.default_rng(w.index)
+    parts = []
+    for lo, hi in w.oracle_rows:
+        n = hi - lo
+        if n <= 2304:
+            parts.append(np.arange(lo, hi))
+        else:
+            parts.append(np.sort(rng.choice(np.arange(lo, hi), size=384, replace=False)))
+            parts.append(np.arange(hi - 128, hi))          # the range's ragged final tile
+    return np.unique(np.concatenate(parts))
+
+
+def assert_attn_close(g, r, what="", mag=None, tol_max=TOL_MAX, tol_mean=TOL_MEAN):
     """Check the kernel's output g against the oracle's r (see the module docstring).
 
     ``mag`` is the oracle's M = P|V| for the same elements; when given it is
@@ -54,4 +84,4 @@ def assert_attn_close(g, r, what="", mag=None):
         msg += f" | e/max(1,P|V|) max {mx:.3e} mean {mean:.3e}"
     log(msg)
     assert np.isfinite(g).all(), f"{what}: non-finite output"
-    assert mx <= TOL_MAX and mean <= TOL_MEAN, f"{what}: max e {mx:.3e}, mean e {mean:.3e}"
+    assert mx <= tol_max and mean <= tol_mean, f"{what}: max e {mx:.3e}, mean e {mean:.3e}"

@@ -30,7 +30,7 @@ def header_functions():
 
 def test_header_symbols_exported():
     declared = header_functions()
-    assert len(declared) == 10, declared
+    assert len(declared) == 11, declared
     out = subprocess.run(["nm", "-D", "--defined-only", qfa.library_path()], stdout=subprocess.PIPE, text=True).stdout
     exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
     missing = [f for f in declared if f not in exported]
@@ -118,6 +118,23 @@ def test_attention_validation():
         assert _attn(**{name: MISALIGNED}) == ALIGN
     assert _attn(sc=FAKE + 2) == ALIGN
     assert _attn(cu=FAKE + 1) == ALIGN
+
+
+def _battn(q=FAKE, k=FAKE, v=FAKE, cu=FAKE, B=1, T=8, H=2, D=128, out=FAKE):
+    return lib.qfa_bf16_varlen_attn(q, k, v, cu, B, T, H, D, out, None)
+
+
+def test_bf16_attention_validation():
+    assert _battn(D=64) == UNSUP
+    assert _battn(H=0) == SHAPE
+    assert _battn(T=-5) == SHAPE
+    assert _battn(B=0) == SHAPE
+    assert _battn(T=1 << 31, H=1) == SHAPE
+    assert _battn(cu=None) == NULL
+    for name in ("q", "k", "v", "out"):
+        assert _battn(**{name: None}) == NULL
+        assert _battn(**{name: MISALIGNED}) == ALIGN
+    assert _battn(cu=FAKE + 1) == ALIGN
 
 
 def test_other_entry_points_validation():

@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import quantized_flash_attn_amd as qfa
-from helpers import assert_attn_close, bf16_to_f32, codes, log
+from helpers import assert_attn_close, bf16_to_f32, codes, log, sample_rows
 from workloads import WORKLOADS, cu_seqlens_tensor, make_qkv, random_qkv
 
 pytestmark = pytest.mark.gpu
@@ -127,26 +127,6 @@ def test_static_without_scales_is_refused():
     assert ei.value.status == 6
 
 
-def _sample_rows(w):
-    """Rows checked at full size: all rows, or seeded samples of the workload's ranges."""
-    if not w.oracle_rows:
-        if w.total_tokens <= 2304:
-            return np.arange(w.total_tokens)
-        step = max(1, w.total_tokens // 1024)
-        return np.unique(np.concatenate([np.arange(0, w.total_tokens, step),
-                                         np.arange(w.total_tokens - 128, w.total_tokens)]))
-    rng = np.random.default_rng(w.index)
-    parts = []
-    for lo, hi in w.oracle_rows:
-        n = hi - lo
-        if n <= 2304:
-            parts.append(np.arange(lo, hi))
-        else:
-            parts.append(np.sort(rng.choice(np.arange(lo, hi), size=384, replace=False)))
-            parts.append(np.arange(hi - 128, hi))          # the range's ragged final tile
-    return np.unique(np.concatenate(parts))
-
-
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("widx", [1, 2, 3, 4, 5])
 def test_workload_attention(widx):
@@ -175,7 +155,7 @@ def test_workload_attention(widx):
     cu_list = w.cu_seqlens
     out = qfa.fp8_varlen_attn(gq8, gk8, gv8, qfa.descale(st), cu_seqlens_tensor(w.seqlens, DEV), w.num_heads)
     torch.cuda.synchronize()
-    rows = _sample_rows(w)
+    rows = sample_rows(w)
     cu = np.array(cu_list)
     seqs = np.unique(np.searchsorted(cu, rows, side="right") - 1)
     log(f"  checking {rows.size} rows in sequences {seqs.tolist()}")

@@ -7,6 +7,8 @@
 * Brute force: plain Python loops (math.exp) on tiny inputs.
 * Against unquantized float64 attention on the bf16 inputs (relative
   Frobenius error within the few-percent E4M3 error; catches swapped scales).
+* The float-input variant (BF16 baseline) against torch-CPU float64 SDPA
+  directly, and against the code variant on decoded values.
 * Invariants: rows of P sum to one (V = 1 gives O = 1), a one-token sequence
   returns its V row, identical keys return the mean of V, no leakage across
   cu_seqlens boundaries, key/value permutation within a sequence.
@@ -18,6 +20,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from oracle import ScaleState, attention, attention_rows, decode, quantize_qkv
 from workloads import random_qkv
 
@@ -205,3 +208,33 @@ def test_magnitude_scale():
     rows = np.array([0, 39, 40, 48])
     o_r, m_r = attention_rows(q8, k8, v8, descale, cu, rows, magnitude=True)
     assert np.abs(o_r - out[rows]).max() <= 1e-12 and np.abs(m_r - mag[rows]).max() <= 1e-12
+
+
+def test_float_attention_equals_torch_sdpa():
+    """The float-input definition (BF16 baseline) against torch-CPU float64 SDPA, per sequence."""
+    rng = np.random.default_rng(31)
+    seqlens = [1, 5, 0, 70, 33]
+    T, H = sum(seqlens), 3
+    q, k, v = (rng.standard_normal((T, H, 128)) * s for s in (2.0, 1.5, 1.0))
+    cu = _cu(seqlens)
+    got, mag = oracle.attention_float(q, k, v, cu, magnitude=True)
+    ref = _sdpa64(q, k, v, cu)
+    assert np.allclose(got, ref, rtol=0, atol=1e-12)
+    assert np.all(mag >= np.abs(got) - 1e-12)
+    rows = np.array([0, 3, 6, 40, 108])
+    sub = oracle.attention_float_rows(q, k, v, cu, rows)
+    assert np.allclose(sub, got[rows], rtol=0, atol=1e-12)
+
+
+def test_float_attention_matches_code_attention_on_decoded_values():
+    """attention(codes) is attention_float of the decoded, scaled codes (same definition)."""
+    rng = np.random.default_rng(8)
+    seqlens = [9, 40]
+    T, H = sum(seqlens), 2
+    codes = [rng.integers(0, 256, (T, H, 128)).astype(np.uint8) for _ in range(3)]
+    for c in codes:
+        c[(c & 0x7F) == 0x7F] = 0x38                      # no NaN codes
+    descale = np.array([0.5, 0.25, 2.0], np.float32)
+    a = oracle.attention(*codes, descale, _cu(seqlens))
+    f = oracle.attention_float(*(oracle.decode(c) * float(d) for c, d in zip(codes, descale)), _cu(seqlens))
+    assert np.array_equal(a, f)
