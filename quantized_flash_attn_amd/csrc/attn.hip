@@ -29,6 +29,8 @@
 //            slot 1          slot 2          slot 3          slot 4
 //   A    S_t = K_t Q^T    p_t = 2^(..)    split p_t       O += P_t V_t
 //   B    split p_{t-1}    O += P V_{t-1}  S_t = K_t Q^T   p_t = 2^(..)
+// (the last quarter of the exponentials of a tile runs with its split, which
+// evens out the VALU work of the two groups).
 //
 //   S = K Q^T       bf16 MFMA on the exactly converted codes (every E4M3 value
 //                   is a bf16 value).  gfx950's fp8 MFMAs add each group of
@@ -206,12 +208,20 @@ __device__ __forceinline__ v2i split4(const v4f& p) {
     return v2i{h, l};
 }
 
+// The softmax step of a key tile is split over two slots to even out the
+// VALU work of the two groups: softmax_head (mask, row max, rescale, and p
+// of key blocks [0, kSplit)) and, in the next slot, the remaining key
+// blocks followed by the hi/lo split.
+constexpr int kSplit = 6;
+
 // P^T operands: phi[qb] / plo[qb] hold the hi / lo codes of keys
 // 16kb + 4g + i (dword kb, byte i) of query r16.  l accumulates the
 // unquantized p in fp32: normalising by the quantized weights instead would
 // drop the mass of the many p below E4M3's subnormal quantum (hi + lo rounds
 // them to 0), a bias that would scale the whole output row.
-__device__ __forceinline__ void split_phase(const v4f (&p)[8][kQB], v8i (&phi)[kQB], v8i (&plo)[kQB], float (&l)[kQB]) {
+__device__ __forceinline__ void split_phase(const Wave& w, v4f (&p)[8][kQB], int nk, v8i (&phi)[kQB], v8i (&plo)[kQB],
+                                            float (&l)[kQB]) {
+    exp_blocks<kSplit, 8>(w, p, nk);
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
         float sum = 0.0f;
@@ -244,9 +254,11 @@ __device__ __forceinline__ void pv_phase(Wave& w, const unsigned char* smem, int
 // The key loop of one wave group.  Period t (t = 0..nt) has four slots
 // separated by workgroup barriers:
 //            slot 1             slot 2          slot 3             slot 4
-//   A (kB=0) S_t = K_t Q^T      p_t             split p_t, K_{t+1}  O += P_t V_t
-//   B (kB=1) split p_{t-1},     O += P V_{t-1}  S_t = K_t Q^T       p_t
-//            K_{t+1} (half 0)                   (half 1 by A)
+//   A (kB=0) S_t = K_t Q^T      p_t (head)      p_t (tail), split, O += P_t V_t
+//                                               K_{t+1} (half 1)
+//   B (kB=1) p_{t-1} (tail),    O += P V_{t-1}  S_t = K_t Q^T       p_t (head)
+//            split, K_{t+1}
+//            (half 0)
 // Loads: K8_{t+2} at slot 1 (lands by the end of slot 2), V_{t+1} at slot 3
 // (lands by the end of slot 4).  Buffer lifetimes: Kb_t is read in slots 1
 // (A) and 3 (B) of period t and rewritten with K_{t+2} during period t+1;
@@ -261,18 +273,19 @@ __device__ __forceinline__ void key_loop(Wave& w, unsigned char* smem) {
     for (int t = 0; t <= nt; ++t) {
         const int cur = t & 1, prev = cur ^ 1;
         const int nk_t = (t + 1 < nt) ? kBN : w.nk_last;   // valid keys of tile t (t < nt)
+        const int nk_p = (t < nt) ? kBN : w.nk_last;       // valid keys of tile t - 1 (t >= 1)
         // slot 1
         if (t + 2 < nt) w.load_k(lds, t + 2, cur);
         if constexpr (!kB) {
             if (t < nt) qk_phase(w, smem, cur, s);
         } else {
-            if (t >= 1) split_phase(s, phi, plo, w.l);
+            if (t >= 1) split_phase(w, s, nk_p, phi, plo, w.l);
             if (t + 1 < nt) w.convert_half(smem, prev, 0);
         }
         __syncthreads();
         // slot 2
         if constexpr (!kB) {
-            if (t < nt) exp_phase(w, s, nk_t);
+            if (t < nt) softmax_head<kSplit>(w, s, nk_t);
         } else {
             if (t >= 1) pv_phase(w, smem, prev, phi, plo);
         }
@@ -281,7 +294,7 @@ __device__ __forceinline__ void key_loop(Wave& w, unsigned char* smem) {
         // slot 3
         if (t + 1 < nt) w.load_v(lds, t + 1, prev);
         if constexpr (!kB) {
-            if (t < nt) split_phase(s, phi, plo, w.l);
+            if (t < nt) split_phase(w, s, nk_t, phi, plo, w.l);
             if (t + 1 < nt) w.convert_half(smem, prev, 1);
         } else {
             if (t < nt) qk_phase(w, smem, cur, s);
@@ -291,7 +304,7 @@ __device__ __forceinline__ void key_loop(Wave& w, unsigned char* smem) {
         if constexpr (!kB) {
             if (t < nt) pv_phase(w, smem, cur, phi, plo);
         } else {
-            if (t < nt) exp_phase(w, s, nk_t);
+            if (t < nt) softmax_head<kSplit>(w, s, nk_t);
         }
         wait_async_loads();
         __syncthreads();

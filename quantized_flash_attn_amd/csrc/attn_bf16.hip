@@ -110,25 +110,43 @@ struct Wave {
 };
 
 // S = K Q^T for one key tile: s[kb][qb] holds keys 16kb + 4g + i of query r16.
+// The K operands of block kb + 1 are requested before the MFMAs of block kb
+// issue (the scheduling fence keeps them there), so LDS latency overlaps
+// the matrix work.
 __device__ __forceinline__ void qk_phase(const Wave& w, const unsigned char* smem, int buf, v4f (&s)[8][kQB]) {
     const unsigned char* kbase = smem + kLdsK + buf * kTileBytes;
+    bf16x8 kop[2][4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) kop[0][c] = *(const bf16x8*)(kbase + (w.k_rd ^ (uint32_t)(c << 4)));
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
+        if (kb + 1 < 8) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                kop[(kb + 1) & 1][c] = *(const bf16x8*)(kbase + (w.k_rd ^ (uint32_t)(c << 4)) + (kb + 1) * 16 * kRow);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb) s[kb][qb] = v4f{0, 0, 0, 0};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const bf16x8 kop = *(const bf16x8*)(kbase + (w.k_rd ^ (uint32_t)(c << 4)) + kb * 16 * kRow);
+        for (int c = 0; c < 4; ++c)
 #pragma unroll
-            for (int qb = 0; qb < kQB; ++qb) s[kb][qb] = mfma_bf16(kop, w.q[qb][c], s[kb][qb]);
-        }
+            for (int qb = 0; qb < kQB; ++qb) s[kb][qb] = mfma_bf16(kop[kb & 1][c], w.q[qb][c], s[kb][qb]);
     }
 }
+
+// The softmax step of a key tile is split over two slots to even out the
+// VALU work of the two groups: softmax_head (mask, row max, rescale, and p
+// of key blocks [0, kSplit)) and, in the next slot, the remaining key
+// blocks followed by the P^T operands.
+constexpr int kSplit = 5;
 
 // P^T operands: pop[qb][j] holds p of keys 32j + 4g + i (elements 0..3) and
 // 32j + 16 + 4g + i (elements 4..7) of query r16, rounded to bf16; l
 // accumulates the fp32 p.
-__device__ __forceinline__ void pack_phase(const v4f (&p)[8][kQB], bf16x8 (&pop)[kQB][4], float (&l)[kQB]) {
+__device__ __forceinline__ void pack_phase(const Wave& w, v4f (&p)[8][kQB], int nk, bf16x8 (&pop)[kQB][4],
+                                           float (&l)[kQB]) {
+    exp_blocks<kSplit, 8>(w, p, nk);
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
         float sum = 0.0f;
@@ -160,8 +178,9 @@ __device__ __forceinline__ void pv_phase(Wave& w, const unsigned char* smem, int
 // The key loop of one wave group.  Period t (t = 0..nt) has four slots
 // separated by workgroup barriers:
 //            slot 1             slot 2          slot 3             slot 4
-//   A (kB=0) S_t = K_t Q^T      p_t             pack p_t           O += P_t V_t
-//   B (kB=1) pack p_{t-1}       O += P V_{t-1}  S_t = K_t Q^T       p_t
+//   A (kB=0) S_t = K_t Q^T      p_t (head)      p_t (tail), pack   O += P_t V_t
+//   B (kB=1) p_{t-1} (tail),    O += P V_{t-1}  S_t = K_t Q^T       p_t (head)
+//            pack
 // Loads: K_{t+1} at slot 1 (lands by the end of slot 2), V_{t+1} at slot 3
 // (lands by the end of slot 4).  Buffer lifetimes: K_t is read in slots 1
 // (A) and 3 (B) of period t and rewritten with K_{t+2} at slot 1 of period
@@ -176,17 +195,18 @@ __device__ __forceinline__ void key_loop(Wave& w, unsigned char* smem) {
     for (int t = 0; t <= nt; ++t) {
         const int cur = t & 1, prev = cur ^ 1;
         const int nk_t = (t + 1 < nt) ? kBN : w.nk_last;   // valid keys of tile t (t < nt)
+        const int nk_p = (t < nt) ? kBN : w.nk_last;       // valid keys of tile t - 1 (t >= 1)
         // slot 1
         if (t + 1 < nt) w.load_k(lds, t + 1, prev);
         if constexpr (!kB) {
             if (t < nt) qk_phase(w, smem, cur, s);
         } else {
-            if (t >= 1) pack_phase(s, pop, w.l);
+            if (t >= 1) pack_phase(w, s, nk_p, pop, w.l);
         }
         __syncthreads();
         // slot 2
         if constexpr (!kB) {
-            if (t < nt) exp_phase(w, s, nk_t);
+            if (t < nt) softmax_head<kSplit>(w, s, nk_t);
         } else {
             if (t >= 1) pv_phase(w, smem, prev, pop);
         }
@@ -195,7 +215,7 @@ __device__ __forceinline__ void key_loop(Wave& w, unsigned char* smem) {
         // slot 3
         if (t + 1 < nt) w.load_v(lds, t + 1, prev);
         if constexpr (!kB) {
-            if (t < nt) pack_phase(s, pop, w.l);
+            if (t < nt) pack_phase(w, s, nk_t, pop, w.l);
         } else {
             if (t < nt) qk_phase(w, smem, cur, s);
         }
@@ -204,7 +224,7 @@ __device__ __forceinline__ void key_loop(Wave& w, unsigned char* smem) {
         if constexpr (!kB) {
             if (t < nt) pv_phase(w, smem, cur, pop);
         } else {
-            if (t < nt) exp_phase(w, s, nk_t);
+            if (t < nt) softmax_head<kSplit>(w, s, nk_t);
         }
         wait_async_loads();
         __syncthreads();

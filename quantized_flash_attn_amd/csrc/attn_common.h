@@ -85,14 +85,42 @@ __device__ inline int xcd_remap(int bid, int nwg) {
     return x * q + min(x, r) + k;
 }
 
-// Scores -> probabilities p = 2^(S c + 8 - m c) for one key tile with nk
-// valid keys.  s[kb][qb] holds keys 16kb + 4g + i of query r16 (lane
-// (r16, g), g4 = 4g).  If the tile's row max exceeds m by more than the
-// slack anywhere in the wave, m moves to it for every query and O and l
-// (which hold the earlier tiles) are rescaled.  W carries m[kQB], l[kQB],
+// p = 2^(S c + 8 - m c) for key blocks [kLo, kHi) of one key tile with nk
+// valid keys, after softmax_head has masked the tile and settled m.  p of
+// masked keys is exactly 0 (also where c = 0 made -inf * c a NaN).
+template <int kLo, int kHi, class W>
+__device__ __forceinline__ void exp_blocks(const W& w, v4f (&s)[8][kQB], int nk) {
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+        const float bias = 8.0f - w.m[qb] * w.cexp;
+#pragma unroll
+        for (int kb = kLo; kb < kHi; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                s[kb][qb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][i], w.cexp, bias));
+    }
+    if (nk < kBN) {
+#pragma unroll
+        for (int kb = kLo; kb < kHi; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool dead = w.g4 >= nk - 16 * kb - i;
+#pragma unroll
+                for (int qb = 0; qb < kQB; ++qb) s[kb][qb][i] = dead ? 0.0f : s[kb][qb][i];
+            }
+    }
+}
+
+// Online-softmax step for one key tile with nk valid keys, first part:
+// mask the keys past nk, take the row max, and, if it exceeds the running
+// max m by more than the slack anywhere in the wave, move m to it for every
+// query and rescale O and l (which hold the earlier tiles).  Then turn the
+// scores of key blocks [0, kSplit) into p = 2^(S c + 8 - m c); the rest
+// follow with exp_blocks<kSplit, 8>.  s[kb][qb] holds keys 16kb + 4g + i of
+// query r16 (lane (r16, g), g4 = 4g).  W carries m[kQB], l[kQB],
 // o[8][kQB], cexp and g4.
-template <class W>
-__device__ __forceinline__ void exp_phase(W& w, v4f (&s)[8][kQB], int nk) {
+template <int kSplit, class W>
+__device__ __forceinline__ void softmax_head(W& w, v4f (&s)[8][kQB], int nk) {
     if (nk < kBN) {
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb)
@@ -125,26 +153,13 @@ __device__ __forceinline__ void exp_phase(W& w, v4f (&s)[8][kQB], int nk) {
             for (int db = 0; db < 8; ++db) w.o[db][qb] *= alpha;
         }
     }
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-        const float bias = 8.0f - w.m[qb] * w.cexp;
-#pragma unroll
-        for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                s[kb][qb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][i], w.cexp, bias));
-    }
-    if (nk < kBN) {
-        // p of masked keys is exactly 0 (also where c = 0 made -inf * c a NaN)
-#pragma unroll
-        for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool dead = w.g4 >= nk - 16 * kb - i;
-#pragma unroll
-                for (int qb = 0; qb < kQB; ++qb) s[kb][qb][i] = dead ? 0.0f : s[kb][qb][i];
-            }
-    }
+    exp_blocks<0, kSplit>(w, s, nk);
+}
+
+// The whole step in one piece.
+template <class W>
+__device__ __forceinline__ void exp_phase(W& w, v4f (&s)[8][kQB], int nk) {
+    softmax_head<8>(w, s, nk);
 }
 
 }  // namespace attn
