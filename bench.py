@@ -176,7 +176,7 @@ def cpu_baseline(w, xs_host, descale_inv, rows):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_seq8192_h16.json")
-ATTN_SRC = os.path.join(ROOT, "quantized_flash_attn_amd", "csrc", "attn.hip")
+ATTN_SRCS = ("attn.hip", "attn_common.h")     # the attention kernel's sources
 
 
 def measured_traffic(workload_index):
@@ -190,9 +190,10 @@ def measured_traffic(workload_index):
         return None
     with open(TRAFFIC_FILE) as f:
         rec = json.load(f)
-    with open(ATTN_SRC, "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != rec["sources_sha256"]["attn.hip"]:
-            return None
+    for name in ATTN_SRCS:
+        with open(os.path.join(ROOT, "quantized_flash_attn_amd", "csrc", name), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != rec["sources_sha256"].get(name):
+                return None
     return rec["kernels"]["attn_fwd_kernel"]["traffic_bytes"]
 
 
