@@ -45,7 +45,74 @@ def parse():
     p.add_argument("--graph-overhead", action="store_true",
                    help="instead of the benchmark, compare eager launches with HIP-graph replay of the whole "
                         "path on the small workloads (1x256 tokens x 2 heads, 1x2304 tokens x 16 heads)")
+    p.add_argument("--packed-head-dim", type=int, default=0,
+                   help="instead of the benchmark, time the fused-QKV path at this head dim (8..128, step 8): "
+                        "quantize from [T, 3, H, D] to padded codes, then FP8 attention writing [T, H, D]")
     return p.parse_args()
+
+
+def packed_path(head_dim, steps, warmup):
+    """Fused QKV projection output -> padded codes -> attention, at 1 x 8192 tokens, 16 heads of head_dim dims.
+
+    Compared with what the unfused path has to do first: split Q, K, V out of the projection output and pad
+    each to 128 dims (three copies), then quantize the three tensors.  Prints one JSON line."""
+    import torch
+
+    import quantized_flash_attn_amd as qfa
+    from workloads import WORKLOADS, cu_seqlens_tensor, make_qkv
+
+    w = WORKLOADS[3]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    H, T, D = w.num_heads, w.total_tokens, head_dim
+    stream = torch.cuda.current_stream(dev)
+    sets = []
+    for i in range(4):
+        q, k, v = make_qkv(w, i, device=dev)
+        sets.append(torch.stack([q[..., :D], k[..., :D], v[..., :D]], dim=1).contiguous())
+        del q, k, v
+    q8, k8, v8 = (torch.empty((T, H, 128), dtype=torch.uint8, device=dev) for _ in range(3))
+    out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+    padded = [torch.zeros((T, H, 128), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    cu = cu_seqlens_tensor(w.seqlens, dev)
+    st = qfa.init_scale_state(dev)
+    sc = qfa.descale(st)
+
+    def timed(fn, n):
+        for i in range(warmup):
+            fn(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    def unfused(i):
+        x = sets[i % len(sets)]
+        for j in range(3):
+            padded[j][..., :D].copy_(x[:, j])
+        qfa.quantize_qkv(st, "dynamic", *padded, q8, k8, v8)
+
+    ms_packed = timed(lambda i: qfa.quantize_qkv_packed(st, "dynamic", sets[i % len(sets)], q8, k8, v8), steps)
+    ms_unfused = timed(unfused, steps)
+    qfa.quantize_qkv_packed(st, "dynamic", sets[0], q8, k8, v8)
+    ms_attn = timed(lambda i: qfa.fp8_varlen_attn(q8, k8, v8, sc, cu, H, head_dim=D, out=out), steps)
+    n_real = T * H * D
+    # amax reads 2 B per real element; quantize reads 2 B per real element and writes 1 B per padded element
+    packed_bytes = 3 * (2 * n_real + 2 * n_real + T * H * 128)
+    flop = 2 * 2 * sum(n * n for n in w.seqlens) * H * D
+    print(json.dumps({"packed_path": {
+        "workload": f"1x{T} tokens, {H} heads, head_dim {D} (codes padded to 128)",
+        "quantize_packed_dynamic": {"ms": round(ms_packed, 4), "algorithmic_bytes": packed_bytes,
+                                    "gbs": round(packed_bytes / (ms_packed * 1e-3) / 1e9, 1),
+                                    "frac_hbm_peak": round(packed_bytes / (ms_packed * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "unfused_split_pad_then_quantize": {"ms": round(ms_unfused, 4)},
+        "attention": {"ms": round(ms_attn, 4), "flop": flop, "tflops": round(flop / (ms_attn * 1e-3) / 1e12, 1)},
+        "step_ms": round(ms_packed + ms_attn, 4),
+        "steps": steps}}), flush=True)
 
 
 def graph_overhead(steps):
@@ -204,6 +271,9 @@ def main():
         return
     if args.graph_overhead:
         graph_overhead(args.steps)
+        return
+    if args.packed_head_dim:
+        packed_path(args.packed_head_dim, args.steps, args.warmup)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))

@@ -13,7 +13,10 @@
  *
  * Conventions for every entry point:
  *   - Tensors are contiguous, token-major [total_tokens, num_heads, head_dim];
- *     head_dim must be 128.  Q, K and V share num_heads and cu_seqlens.
+ *     head_dim is 128, except where an entry point says otherwise (the
+ *     packed quantize path and the FP8 attention take head dims 8..128 in
+ *     steps of 8 on codes zero-padded to 128).  Q, K and V share num_heads
+ *     and cu_seqlens.
  *   - Device pointers must be 16-byte aligned.  The caller owns all device
  *     memory; the library never allocates device memory.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
@@ -39,7 +42,7 @@ typedef enum qfa_status {
     QFA_OK = 0,
     QFA_ERR_NULL = 1,        /* a required pointer is NULL */
     QFA_ERR_SHAPE = 2,       /* negative/zero/overflowing sizes, bad num_seqs */
-    QFA_ERR_UNSUPPORTED = 3, /* head_dim != 128 */
+    QFA_ERR_UNSUPPORTED = 3, /* head_dim not accepted by the entry point */
     QFA_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned */
     QFA_ERR_MODE = 5,        /* mode is neither QFA_DYNAMIC nor QFA_STATIC */
     QFA_ERR_NO_STATIC = 6,   /* QFA_STATIC on a state initialised without static amax */
@@ -129,19 +132,41 @@ qfa_status qfa_quantize_qkv(const qfa_scale_state* st, int mode, const void* q, 
                             const void* v, int64_t total_tokens, int num_heads, int head_dim,
                             uint8_t* q8, uint8_t* k8, uint8_t* v8, void* stream);
 
+/*
+ * One forward of the quantizer straight from a fused QKV projection output
+ * ([P2] Performance counts the three quantization launches and the head-dim
+ * un-padding among the overheads of small images): same scale-state rules
+ * as qfa_quantize_qkv, with
+ *   qkv          device bf16 [total_tokens, 3, num_heads, head_dim]
+ *                (Q = qkv[:, 0], K = qkv[:, 1], V = qkv[:, 2])
+ *   head_dim     8..128 in steps of 8 (e.g. 80 or 72 for ViT encoders
+ *                whose hidden size is not 128 * num_heads)
+ *   q8, k8, v8   device uint8 E4M3 codes [total_tokens, num_heads, 128]
+ *                (out): dims [0, head_dim) are the codes, dims past it 0 --
+ *                the layout qfa_fp8_varlen_attn reads for any head_dim
+ * amax is taken over the head_dim real dims only.  Two launches (dynamic)
+ * or one (static).  total_tokens * num_heads * 16 must be below 2^31.
+ */
+qfa_status qfa_quantize_qkv_packed(const qfa_scale_state* st, int mode, const void* qkv, int64_t total_tokens,
+                                   int num_heads, int head_dim, uint8_t* q8, uint8_t* k8, uint8_t* v8,
+                                   void* stream);
+
 /* Device pointer to float[3] {s_q, s_k, s_v} inside the state (valid after a forward). */
 const float* qfa_descale_ptr(const qfa_scale_state* st);
 
 /*
  * Varlen FP8 attention with per-tensor scales ([P4] Requirements: a
  * per-tensor FP8 varlen attention over packed variable-length image batches).
- *   out[i,h,:] = sum_j softmax_j(s_q*s_k*<q_i,k_j>/sqrt(128)) * s_v * v_j
+ *   out[i,h,:] = sum_j softmax_j(s_q*s_k*<q_i,k_j>/sqrt(head_dim)) * s_v * v_j
  * over the keys j of the sequence that contains token i, non-causal.
- *   q8, k8, v8     device E4M3 codes [total_tokens, num_heads, 128]
+ *   q8, k8, v8     device E4M3 codes [total_tokens, num_heads, 128]; for
+ *                  head_dim < 128 the dims past head_dim must hold code 0
+ *                  (as qfa_quantize_qkv_packed writes them)
  *   scales         device float[3] {s_q, s_k, s_v} (e.g. qfa_descale_ptr)
  *   cu_seqlens     device int32[num_seqs + 1]: cu[0] = 0, non-decreasing,
  *                  cu[num_seqs] = total_tokens; empty sequences are allowed
- *   out            device bf16 [total_tokens, num_heads, 128] (out)
+ *   head_dim       8..128 in steps of 8 (128 for qfa_quantize_qkv's codes)
+ *   out            device bf16 [total_tokens, num_heads, head_dim] (out)
  * total_tokens must be below 2^31.  The kernel uses E4M3 probabilities split
  * into two terms (hi + lo) for the P*V product and float32 accumulation.
  */

@@ -44,7 +44,7 @@ from .scales import (
     scales_from_amax,
     static_amax_eff,
 )
-from .quantize import quantize, quantize_qkv
+from .quantize import quantize, quantize_qkv, quantize_qkv_packed
 from .attention import attention, attention_float, attention_float_rows, attention_rows
 
 __all__ = [
@@ -60,6 +60,7 @@ __all__ = [
     "static_amax_eff",
     "quantize",
     "quantize_qkv",
+    "quantize_qkv_packed",
     "attention",
     "attention_rows",
     "attention_float",

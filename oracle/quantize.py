@@ -5,6 +5,11 @@ the attention call; its Usage and Calibrate-Once sections say where the scales
 come from (see ``oracle.scales``).  Each element becomes
 ``encode(fp32(fp32(x) * inv[t]))``: one float32 multiply, rounded to nearest
 even, then the saturating E4M3 encoding of ``oracle.e4m3``.
+
+``quantize_qkv_packed`` takes the fused QKV projection output ``[T, 3, H, D]``
+("FP8 ViT Encoder Attention", Performance, counts the split into three
+quantization launches and the head-dim un-padding among the overheads) and
+returns codes padded with zeros to 128 dims; the amax covers the D real dims.
 """
 
 import numpy as np
@@ -35,3 +40,25 @@ def quantize_qkv(state, mode: str, q, k, v) -> tuple:
     else:
         raise ValueError("mode must be 'dynamic' or 'static'")
     return quantize(q, inv[0]), quantize(k, inv[1]), quantize(v, inv[2]), descale, observed
+
+
+PADDED_DIM = 128
+
+
+def quantize_qkv_packed(state, mode: str, qkv) -> tuple:
+    """One forward on a float32 array ``[T, 3, H, D]`` of bf16 values (D <= 128).
+
+    Q, K, V are ``qkv[:, 0]``, ``qkv[:, 1]``, ``qkv[:, 2]``.  Returns ``(q8, k8,
+    v8, descale, observed)`` with codes ``[T, H, 128]`` whose dims past D are 0.
+    """
+    qkv = np.asarray(qkv, dtype=np.float32)
+    T, three, H, D = qkv.shape
+    if three != 3 or D > PADDED_DIM:
+        raise ValueError("qkv must be [T, 3, H, D] with D <= 128")
+    q8, k8, v8, descale, observed = quantize_qkv(state, mode, qkv[:, 0], qkv[:, 1], qkv[:, 2])
+    padded = []
+    for c in (q8, k8, v8):
+        p = np.zeros((T, H, PADDED_DIM), dtype=np.uint8)
+        p[:, :, :D] = c
+        padded.append(p)
+    return padded[0], padded[1], padded[2], descale, observed

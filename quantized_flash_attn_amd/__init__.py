@@ -12,8 +12,12 @@ Entry points (same names as the C ABI without the ``qfa_`` prefix):
 * ``init_scale_state(device=..., history_len=16, static_amax=None, margin=1.5)``
   -> ``ScaleState``
 * ``quantize_qkv(state, mode, q, k, v, q8=None, k8=None, v8=None)`` -> ``(q8, k8, v8)``
+* ``quantize_qkv_packed(state, mode, qkv, q8=None, k8=None, v8=None)`` -> ``(q8, k8, v8)``:
+  from a fused projection output ``[T, 3, H, D]``, D in 8..128 (step 8), to codes
+  ``[T, H, 128]`` zero-padded past D
 * ``descale(state)`` -> device float32[3] view {s_q, s_k, s_v}
-* ``fp8_varlen_attn(q8, k8, v8, scales, cu_seqlens, num_heads, head_dim=128, out=None)``
+* ``fp8_varlen_attn(q8, k8, v8, scales, cu_seqlens, num_heads, head_dim=128, out=None)``:
+  codes ``[T, H, 128]``; output ``[T, H, head_dim]``
 * ``bf16_varlen_attn(q, k, v, cu_seqlens, num_heads, head_dim=128, out=None)`` (the BF16 baseline)
 * ``read_scale_state(state)`` -> dict (synchronises; for tests and checkpoints)
 * ``check_cu_seqlens(cu_seqlens, total_tokens)`` (synchronises)
@@ -95,6 +99,7 @@ def _load():
         "qfa_scale_state_bytes": (ctypes.c_size_t, []),
         "qfa_init_scale_state": (i32, [ctypes.POINTER(_State), vp, i32, ctypes.POINTER(ctypes.c_float), f32, vp]),
         "qfa_quantize_qkv": (i32, [ctypes.POINTER(_State), i32, vp, vp, vp, i64, i32, i32, vp, vp, vp, vp]),
+        "qfa_quantize_qkv_packed": (i32, [ctypes.POINTER(_State), i32, vp, i64, i32, i32, vp, vp, vp, vp]),
         "qfa_descale_ptr": (vp, [ctypes.POINTER(_State)]),
         "qfa_fp8_varlen_attn": (i32, [vp, vp, vp, vp, vp, i32, i64, i32, i32, vp, vp]),
         "qfa_bf16_varlen_attn": (i32, [vp, vp, vp, vp, i32, i64, i32, i32, vp, vp]),
@@ -118,6 +123,7 @@ EXPORTS = (
     "qfa_scale_state_bytes",
     "qfa_init_scale_state",
     "qfa_quantize_qkv",
+    "qfa_quantize_qkv_packed",
     "qfa_descale_ptr",
     "qfa_fp8_varlen_attn",
     "qfa_bf16_varlen_attn",
@@ -226,6 +232,27 @@ def quantize_qkv(state: ScaleState, mode, q, k, v, q8=None, k8=None, v8=None):
     return tuple(outs)
 
 
+def quantize_qkv_packed(state: ScaleState, mode, qkv, q8=None, k8=None, v8=None):
+    """One forward from a fused QKV projection output ``[T, 3, H, D]`` to padded codes ``[T, H, 128]``."""
+    _require_gpu(qkv)
+    if mode not in _MODES:
+        raise ValueError("mode must be 'dynamic' or 'static'")
+    if qkv.dim() != 4 or qkv.shape[1] != 3 or qkv.dtype != torch.bfloat16 or not qkv.is_contiguous():
+        raise ValueError("qkv must be a contiguous bf16 tensor [tokens, 3, heads, head_dim]")
+    T, _, H, D = qkv.shape
+    outs = []
+    for o in (q8, k8, v8):
+        if o is None:
+            o = torch.empty((T, H, HEAD_DIM), dtype=torch.uint8, device=qkv.device)
+        elif o.dtype != torch.uint8 or tuple(o.shape) != (T, H, HEAD_DIM) or not o.is_contiguous():
+            raise ValueError("q8, k8, v8 must be contiguous uint8 tensors [tokens, heads, 128]")
+        outs.append(o)
+    with torch.cuda.device(qkv.device):
+        _check(_lib.qfa_quantize_qkv_packed(state.handle, _MODES[mode], qkv.data_ptr(), T, H, D, outs[0].data_ptr(),
+                                            outs[1].data_ptr(), outs[2].data_ptr(), _stream_ptr(qkv.device)))
+    return tuple(outs)
+
+
 def descale(state: ScaleState) -> torch.Tensor:
     """Device float32[3] {s_q, s_k, s_v}: a view into the state buffer."""
     ptr = _lib.qfa_descale_ptr(state.handle)
@@ -236,22 +263,25 @@ def descale(state: ScaleState) -> torch.Tensor:
 
 
 def fp8_varlen_attn(q8, k8, v8, scales, cu_seqlens, num_heads=None, head_dim=HEAD_DIM, out=None):
-    """bf16 attention output ``[T, H, 128]`` from E4M3 codes and per-tensor scales."""
+    """bf16 attention output ``[T, H, head_dim]`` from E4M3 codes ``[T, H, 128]`` and per-tensor scales.
+
+    For ``head_dim`` below 128 the codes must be zero past ``head_dim`` (``quantize_qkv_packed`` writes them so).
+    """
     _require_gpu(q8, k8, v8, scales, cu_seqlens)
     T, H, D = _qkv_shape(q8)
     if num_heads is not None and num_heads != H:
         raise ValueError("num_heads does not match q8")
     for t in (q8, k8, v8):
-        if t.dtype != torch.uint8 or tuple(t.shape) != (T, H, D) or not t.is_contiguous():
-            raise ValueError("q8, k8, v8 must be contiguous uint8 tensors of one shape")
+        if t.dtype != torch.uint8 or tuple(t.shape) != (T, H, HEAD_DIM) or not t.is_contiguous():
+            raise ValueError("q8, k8, v8 must be contiguous uint8 tensors [tokens, heads, 128]")
     if scales.dtype != torch.float32 or scales.numel() < 3:
         raise ValueError("scales must be float32[3]")
     if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
         raise ValueError("cu_seqlens must be int32[num_seqs + 1]")
     if out is None:
-        out = torch.empty((T, H, D), dtype=torch.bfloat16, device=q8.device)
-    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (T, H, D) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous bf16 tensor of the input shape")
+        out = torch.empty((T, H, head_dim), dtype=torch.bfloat16, device=q8.device)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (T, H, head_dim) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 tensor [tokens, heads, head_dim]")
     with torch.cuda.device(q8.device):
         _check(_lib.qfa_fp8_varlen_attn(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), scales.data_ptr(),
                                         cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, T, H, head_dim,

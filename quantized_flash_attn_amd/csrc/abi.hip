@@ -52,6 +52,9 @@ qfa_status check_shape(int64_t total_tokens, int num_heads, int head_dim, int64_
     return QFA_OK;
 }
 
+// Head dims the padded paths accept: 8..128 in steps of 8 (16-byte bf16 rows).
+bool padded_head_dim_ok(int head_dim) { return head_dim >= 8 && head_dim <= QFA_HEAD_DIM && head_dim % 8 == 0; }
+
 }  // namespace
 
 extern "C" {
@@ -63,7 +66,7 @@ const char* qfa_status_string(qfa_status s) {
         case QFA_OK: return "ok";
         case QFA_ERR_NULL: return "null pointer";
         case QFA_ERR_SHAPE: return "invalid shape";
-        case QFA_ERR_UNSUPPORTED: return "unsupported head_dim (only 128)";
+        case QFA_ERR_UNSUPPORTED: return "unsupported head_dim";
         case QFA_ERR_ALIGN: return "device pointer not 16-byte aligned";
         case QFA_ERR_MODE: return "invalid mode";
         case QFA_ERR_NO_STATIC: return "static mode without static amax";
@@ -137,6 +140,33 @@ qfa_status qfa_quantize_qkv(const qfa_scale_state* st, int mode, const void* q, 
     return check_launch(e, where);
 }
 
+qfa_status qfa_quantize_qkv_packed(const qfa_scale_state* st, int mode, const void* qkv, int64_t total_tokens,
+                                   int num_heads, int head_dim, uint8_t* q8, uint8_t* k8, uint8_t* v8, void* stream) {
+    const char* where = "qfa_quantize_qkv_packed";
+    if (!st) return fail(QFA_ERR_NULL, "%s: null state handle", where);
+    if (st->magic != QFA_STATE_MAGIC || !st->device) return fail(QFA_ERR_STATE, "%s: state not initialised", where);
+    if (mode != QFA_DYNAMIC && mode != QFA_STATIC) return fail(QFA_ERR_MODE, "%s: mode %d", where, mode);
+    if (mode == QFA_STATIC && !st->has_static)
+        return fail(QFA_ERR_NO_STATIC, "%s: state was initialised without static amax", where);
+    if (!padded_head_dim_ok(head_dim))
+        return fail(QFA_ERR_UNSUPPORTED, "%s: head_dim %d (8..128 in steps of 8)", where, head_dim);
+    if (num_heads <= 0) return fail(QFA_ERR_SHAPE, "%s: num_heads %d must be positive", where, num_heads);
+    if (total_tokens < 0) return fail(QFA_ERR_SHAPE, "%s: total_tokens %lld is negative", where, (long long)total_tokens);
+    // 8-code output chunks are indexed in 32 bits
+    if (total_tokens > (INT64_C(1) << 31) / ((int64_t)num_heads * 16) - 1)
+        return fail(QFA_ERR_SHAPE, "%s: tensor too large", where);
+    const bool any = total_tokens > 0;
+    if (any && (!qkv || !q8 || !k8 || !v8)) return fail(QFA_ERR_NULL, "%s: null tensor pointer", where);
+    if (any && !(aligned16(qkv) && aligned16(q8) && aligned16(k8) && aligned16(v8)))
+        return fail(QFA_ERR_ALIGN, "%s: tensor pointer not 16-byte aligned", where);
+    qfa_status s = check_pending(where);
+    if (s != QFA_OK) return s;
+    const hipError_t e = qfa::launch_quantize_packed((qfa::DeviceState*)st->device, mode == QFA_DYNAMIC,
+                                                     (const uint16_t*)qkv, total_tokens, num_heads, head_dim, q8, k8,
+                                                     v8, (hipStream_t)stream);
+    return check_launch(e, where);
+}
+
 const float* qfa_descale_ptr(const qfa_scale_state* st) {
     if (!st || st->magic != QFA_STATE_MAGIC || !st->device) return nullptr;
     return ((const qfa::DeviceState*)st->device)->descale;
@@ -146,8 +176,10 @@ qfa_status qfa_fp8_varlen_attn(const uint8_t* q8, const uint8_t* k8, const uint8
                                const int32_t* cu_seqlens, int num_seqs, int64_t total_tokens, int num_heads,
                                int head_dim, void* out, void* stream) {
     const char* where = "qfa_fp8_varlen_attn";
+    if (!padded_head_dim_ok(head_dim))
+        return fail(QFA_ERR_UNSUPPORTED, "%s: head_dim %d (8..128 in steps of 8)", where, head_dim);
     int64_t n = 0;
-    qfa_status s = check_shape(total_tokens, num_heads, head_dim, &n, where);
+    qfa_status s = check_shape(total_tokens, num_heads, QFA_HEAD_DIM, &n, where);  // code rows are 128 wide
     if (s != QFA_OK) return s;
     if (num_seqs < 1) return fail(QFA_ERR_SHAPE, "%s: num_seqs %d must be at least 1", where, num_seqs);
     if (total_tokens >= (INT64_C(1) << 31)) return fail(QFA_ERR_SHAPE, "%s: total_tokens must be below 2^31", where);
@@ -161,7 +193,7 @@ qfa_status qfa_fp8_varlen_attn(const uint8_t* q8, const uint8_t* k8, const uint8
     if (s != QFA_OK) return s;
     if (n == 0) return ok();
     const hipError_t e = qfa::launch_attention(q8, k8, v8, scales, cu_seqlens, num_seqs, (int)total_tokens, num_heads,
-                                               out, (hipStream_t)stream);
+                                               head_dim, out, (hipStream_t)stream);
     return check_launch(e, where);
 }
 

@@ -7,6 +7,10 @@
 //
 // Inputs are E4M3 codes in HBM (1 byte per element); the kernel works on the
 // code values and folds the per-tensor scales into the softmax and epilogue.
+// Code rows are always 128 dims wide: a head_dim D below 128 arrives
+// zero-padded (the zeros add nothing to Q K^T and give zero output dims),
+// the softmax scale is 1/sqrt(D), and only the D real output dims are
+// written, to rows D wide.
 //
 // Work decomposition
 //   * One workgroup = 8 waves = one (head, 256-query tile of one sequence);
@@ -40,7 +44,7 @@
 //                   The bf16 MFMA sums exactly.  The accumulator gives every
 //                   lane 32 keys of ONE query, so the row max is in-lane plus
 //                   two lane swaps.
-//   online softmax  p = 2^(S c + 8 - m c), c = s_q s_k log2(e) / sqrt(128), m
+//   online softmax  p = 2^(S c + 8 - m c), c = s_q s_k log2(e) / sqrt(D), m
 //                   a running row max that only moves when a tile's max exceeds
 //                   it by more than 0.5 log2 units, so p <= 2^8.5 = 362 < 448
 //                   and most tiles skip the rescale.  The 2^8 shift keeps small
@@ -51,6 +55,8 @@
 //                   in LDS, B = P^T straight from the S accumulator layout.
 //                   l sums the unquantized p in fp32.
 //   epilogue        out = bf16(O * s_v / l).
+
+#include <cmath>
 
 #include "attn_common.h"
 
@@ -314,7 +320,7 @@ __device__ __forceinline__ void key_loop(Wave& w, unsigned char* smem) {
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8, const uint8_t* __restrict__ v8,
     const float* __restrict__ scales, const int32_t* __restrict__ cu, int num_seqs, int num_heads,
-    int tiles_per_head, __bf16* __restrict__ out) {
+    int tiles_per_head, int head_dim, float log2e_rsqrt_d, __bf16* __restrict__ out) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
     lds_u8* const lds = (lds_u8*)smem;
 
@@ -386,7 +392,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
         w.q[qb][3] = codes_to_bf16x8(c[2], c[3]);
     }
     const float s_q = scales[0], s_k = scales[1], s_v = scales[2];
-    w.cexp = s_q * s_k * (kLog2e * kRsqrtD);
+    w.cexp = s_q * s_k * log2e_rsqrt_d;
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
 #pragma unroll
@@ -410,21 +416,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     else
         key_loop<false>(w, smem);
 
-    // ---- epilogue: lane holds O^T[d = 16db + 4g + i][query r16] ----
+    // ---- epilogue: lane holds O^T[d = 16db + 4g + i][query r16]; the output
+    // rows hold head_dim dims (a multiple of 8, so a lane's 4 dims are all
+    // inside or all past it) ----
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
         const int qi = q0 + w.wave * (16 * kQB) + qb * 16 + r16;
         if (qi < seq_hi) {
             const float f = s_v / quad_sum(w.l[qb]);
-            __bf16* dst = out + (size_t)qi * w.row_stride + (size_t)h * kD + 4 * g;
+            __bf16* dst = out + ((size_t)qi * num_heads + h) * head_dim + 4 * g;
 #pragma unroll
             for (int db = 0; db < 8; ++db) {
-                bf16x4 r;
-                r[0] = (__bf16)(w.o[db][qb][0] * f);
-                r[1] = (__bf16)(w.o[db][qb][1] * f);
-                r[2] = (__bf16)(w.o[db][qb][2] * f);
-                r[3] = (__bf16)(w.o[db][qb][3] * f);
-                *(bf16x4*)(dst + 16 * db) = r;
+                if (16 * db + 4 * g < head_dim) {
+                    bf16x4 r;
+                    r[0] = (__bf16)(w.o[db][qb][0] * f);
+                    r[1] = (__bf16)(w.o[db][qb][1] * f);
+                    r[2] = (__bf16)(w.o[db][qb][2] * f);
+                    r[3] = (__bf16)(w.o[db][qb][3] * f);
+                    *(bf16x4*)(dst + 16 * db) = r;
+                }
             }
         }
     }
@@ -433,14 +443,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
 }  // namespace
 
 hipError_t launch_attention(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* scales,
-                            const int32_t* cu_seqlens, int num_seqs, int total_tokens, int num_heads, void* out,
-                            hipStream_t s) {
+                            const int32_t* cu_seqlens, int num_seqs, int total_tokens, int num_heads, int head_dim,
+                            void* out, hipStream_t s) {
     const int tph = tiles_per_head(total_tokens, num_seqs);
     const long long nwg = (long long)tph * num_heads;
     if (nwg <= 0) return hipSuccess;
     if (nwg > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+    // log2(e) / sqrt(head_dim) in float32: for head_dim 128 this is the
+    // product of the two float32 constants, as before.
+    const float rsqrt_d = head_dim == kD ? kRsqrtD : (float)(1.0 / std::sqrt((double)head_dim));
     attn_fwd_kernel<<<(unsigned)nwg, kThreads, 0, s>>>(q8, k8, v8, scales, cu_seqlens, num_seqs, num_heads,
-                                                       tph, (__bf16*)out);
+                                                       tph, head_dim, kLog2e * rsqrt_d, (__bf16*)out);
     return hipGetLastError();
 }
 

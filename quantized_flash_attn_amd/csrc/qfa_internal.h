@@ -35,8 +35,12 @@ hipError_t launch_quantize_dynamic(DeviceState* st, const uint16_t* q, const uin
                                    int64_t n, uint8_t* q8, uint8_t* k8, uint8_t* v8, hipStream_t s);
 hipError_t launch_quantize_static(DeviceState* st, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                   int64_t n, uint8_t* q8, uint8_t* k8, uint8_t* v8, hipStream_t s);
+hipError_t launch_quantize_packed(DeviceState* st, bool dynamic, const uint16_t* qkv, int64_t total_tokens,
+                                  int num_heads, int head_dim, uint8_t* q8, uint8_t* k8, uint8_t* v8, hipStream_t s);
+// q8, k8, v8: [total_tokens, num_heads, 128] codes, zero past head_dim;
+// out: [total_tokens, num_heads, head_dim] bf16.
 hipError_t launch_attention(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* scales,
-                            const int32_t* cu_seqlens, int num_seqs, int total_tokens, int num_heads,
+                            const int32_t* cu_seqlens, int num_seqs, int total_tokens, int num_heads, int head_dim,
                             void* out, hipStream_t s);
 hipError_t launch_attention_bf16(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
                                  int num_seqs, int total_tokens, int num_heads, void* out, hipStream_t s);

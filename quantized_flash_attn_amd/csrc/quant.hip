@@ -18,6 +18,14 @@
 //                          from the ring itself (all workgroups compute the
 //                          same value); workgroup (0, t) is the only writer of
 //                          ring slot, cursor and scales.  No atomics.
+//   amax_packed_kernel,    the same two steps reading Q, K and V straight out
+//   quantize_packed_kernel of a fused QKV projection output [T, 3, H, D]
+//                          (D <= 128) and writing codes [T, H, 128] whose dims
+//                          past D are zero, the layout the attention kernel
+//                          reads.  This replaces the split into three tensors
+//                          and the head-dim padding that "FP8 ViT Encoder
+//                          Attention" (Performance) counts among the costs of
+//                          small images.
 
 #include "qfa_internal.h"
 
@@ -231,6 +239,96 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(DeviceState* st, con
     for (; i < n_chunks; i += stride) __builtin_nontemporal_store(quantize8(__builtin_nontemporal_load(src + i), inv), dst + i);
 }
 
+// Packed input: tensor t's chunk i (8 consecutive bf16 of one head row) is
+// chunk (token * 3 + t) * cpr + w of the [T, 3, H, D] array, with
+// token = i / cpr, w = i % cpr and cpr = H * D / 8 chunks per (token, tensor).
+__global__ __launch_bounds__(kThreads) void amax_packed_kernel(const u32x4* __restrict__ qkv, uint32_t n_chunks,
+                                                               uint32_t cpr, DeviceState* st) {
+    const int t = blockIdx.y;
+    uint32_t* __restrict__ partial = &st->partial[0][0];
+    if (blockIdx.x == 0 && t == 0 && threadIdx.x == 0) st->cursor_snap = st->cursor;
+    const uint32_t stride = gridDim.x * kThreads;
+    auto src = [&](uint32_t i) {
+        const uint32_t token = i / cpr, w = i - token * cpr;
+        return qkv + ((size_t)token * 3 + t) * cpr + w;
+    };
+    uint32_t m = 0;
+    uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+    // four independent loads in flight per thread (i + 3 stride < n_chunks < 2^31: no overflow)
+    for (; i + 3 * stride < n_chunks; i += 4 * stride) {
+        const u32x4 a = __builtin_nontemporal_load(src(i));
+        const u32x4 b = __builtin_nontemporal_load(src(i + stride));
+        const u32x4 c = __builtin_nontemporal_load(src(i + 2 * stride));
+        const u32x4 d = __builtin_nontemporal_load(src(i + 3 * stride));
+        m = max_abs_bits(a, m);
+        m = max_abs_bits(b, m);
+        m = max_abs_bits(c, m);
+        m = max_abs_bits(d, m);
+    }
+    for (; i < n_chunks; i += stride) m = max_abs_bits(__builtin_nontemporal_load(src(i)), m);
+    m = wave_max_u32(m);
+    __shared__ uint32_t red[kThreads / 64];
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t r = red[0];
+#pragma unroll
+        for (int w = 1; w < kThreads / 64; ++w) r = max(r, red[w]);
+        partial[t * kMaxPartials + blockIdx.x] = r;
+    }
+}
+
+// Output chunk o of tensor t (8 codes) is dims 8 (o & 15) .. + 7 of head row
+// o >> 4 = token * H + h of the [T, H, 128] codes; the first cph = D / 8
+// chunks of a row come from the packed input, the rest are zero.
+template <bool kStatic>
+__global__ __launch_bounds__(kThreads) void quantize_packed_kernel(DeviceState* st, const u32x4* __restrict__ qkv,
+                                                                   uint32_t n_out_chunks, uint32_t num_heads,
+                                                                   uint32_t cph, u32x2* __restrict__ q8,
+                                                                   u32x2* __restrict__ k8, u32x2* __restrict__ v8,
+                                                                   int n_partials) {
+    const int t = blockIdx.y;
+    float inv;
+    if constexpr (kStatic) {
+        const float eff = st->static_eff[t];
+        float d;
+        scales_from_amax(eff, &d, &inv);
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            st->amax_eff[t] = eff;
+            st->descale[t] = d;
+            st->inv[t] = inv;
+        }
+    } else {
+        inv = dynamic_inv(st, t, n_partials);
+    }
+    u32x2* __restrict__ dst = t == 0 ? q8 : (t == 1 ? k8 : v8);
+    const uint32_t cpr = num_heads * cph;
+    const uint32_t stride = gridDim.x * kThreads;
+    // Input chunk of output chunk o (valid when (o & 15) < cph).
+    auto src = [&](uint32_t o) {
+        const uint32_t row = o >> 4, dc = o & 15;
+        const uint32_t token = row / num_heads, h = row - token * num_heads;
+        return qkv + ((size_t)token * 3 + t) * cpr + h * cph + dc;
+    };
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    uint32_t o = blockIdx.x * kThreads + threadIdx.x;
+    // four independent chunks in flight per thread (o + 3 stride < n_out_chunks < 2^31: no overflow)
+    for (; o + 3 * stride < n_out_chunks; o += 4 * stride) {
+        u32x4 x[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t oo = o + r * stride;
+            x[r] = (oo & 15) < cph ? __builtin_nontemporal_load(src(oo)) : zero;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) __builtin_nontemporal_store(quantize8(x[r], inv), dst + o + r * stride);
+    }
+    for (; o < n_out_chunks; o += stride) {
+        const u32x4 x = (o & 15) < cph ? __builtin_nontemporal_load(src(o)) : zero;
+        __builtin_nontemporal_store(quantize8(x, inv), dst + o);
+    }
+}
+
 int grid_for(int64_t n_chunks, int64_t chunks_per_thread, int cap) {
     int64_t g = (n_chunks + kThreads * chunks_per_thread - 1) / (kThreads * chunks_per_thread);
     if (g < 1) g = 1;
@@ -258,6 +356,32 @@ hipError_t launch_quantize_dynamic(DeviceState* st, const uint16_t* q, const uin
     const int gq = grid_for(chunks, 16, 2048);
     quantize_kernel<false><<<dim3(gq, 3), kThreads, 0, s>>>(st, (const u32x4*)q, (const u32x4*)k, (const u32x4*)v,
                                                            chunks, (u32x2*)q8, (u32x2*)k8, (u32x2*)v8, ga);
+    return hipGetLastError();
+}
+
+// qkv: [total_tokens, 3, num_heads, head_dim] bf16 (head_dim a multiple of
+// 8, at most 128); outputs [total_tokens, num_heads, 128] codes.  The caller
+// guarantees total_tokens * num_heads * 16 < 2^31.
+hipError_t launch_quantize_packed(DeviceState* st, bool dynamic, const uint16_t* qkv, int64_t total_tokens,
+                                  int num_heads, int head_dim, uint8_t* q8, uint8_t* k8, uint8_t* v8, hipStream_t s) {
+    const uint32_t cph = (uint32_t)head_dim / 8;
+    const uint32_t cpr = (uint32_t)num_heads * cph;
+    const uint32_t in_chunks = (uint32_t)total_tokens * cpr;            // per tensor
+    const uint32_t out_chunks = (uint32_t)total_tokens * (uint32_t)num_heads * 16;
+    int ga = 1;
+    if (dynamic) {
+        ga = grid_for(in_chunks, 8, kMaxPartials);
+        amax_packed_kernel<<<dim3(ga, 3), kThreads, 0, s>>>((const u32x4*)qkv, in_chunks, cpr, st);
+    }
+    const int gq = grid_for(out_chunks, 16, 2048);
+    if (dynamic)
+        quantize_packed_kernel<false><<<dim3(gq, 3), kThreads, 0, s>>>(st, (const u32x4*)qkv, out_chunks,
+                                                                       (uint32_t)num_heads, cph, (u32x2*)q8,
+                                                                       (u32x2*)k8, (u32x2*)v8, ga);
+    else
+        quantize_packed_kernel<true><<<dim3(gq, 3), kThreads, 0, s>>>(st, (const u32x4*)qkv, out_chunks,
+                                                                      (uint32_t)num_heads, cph, (u32x2*)q8,
+                                                                      (u32x2*)k8, (u32x2*)v8, 1);
     return hipGetLastError();
 }
 

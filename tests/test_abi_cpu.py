@@ -30,7 +30,7 @@ def header_functions():
 
 def test_header_symbols_exported():
     declared = header_functions()
-    assert len(declared) == 11, declared
+    assert len(declared) == 12, declared
     out = subprocess.run(["nm", "-D", "--defined-only", qfa.library_path()], stdout=subprocess.PIPE, text=True).stdout
     exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
     missing = [f for f in declared if f not in exported]
@@ -106,7 +106,8 @@ def _attn(q8=FAKE, k8=FAKE, v8=FAKE, sc=FAKE, cu=FAKE, B=1, T=8, H=2, D=128, out
 
 
 def test_attention_validation():
-    assert _attn(D=64) == UNSUP
+    for d in (0, 4, 100, 136, 256):
+        assert _attn(D=d) == UNSUP, d
     assert _attn(H=0) == SHAPE
     assert _attn(T=-5) == SHAPE
     assert _attn(B=0) == SHAPE
@@ -118,6 +119,31 @@ def test_attention_validation():
         assert _attn(**{name: MISALIGNED}) == ALIGN
     assert _attn(sc=FAKE + 2) == ALIGN
     assert _attn(cu=FAKE + 1) == ALIGN
+
+
+def _packed(h, mode=0, qkv=FAKE, T=8, H=2, D=80, outs=(FAKE,) * 3):
+    return lib.qfa_quantize_qkv_packed(h, mode, qkv, T, H, D, outs[0], outs[1], outs[2], None)
+
+
+def test_packed_quantize_validation():
+    assert _packed(None) == NULL
+    assert _packed(ctypes.byref(_handle(magic=0))) == STATE
+    h = _handle()
+    assert _packed(ctypes.byref(h), mode=3) == MODE
+    assert _packed(ctypes.byref(h), mode=1) == NO_STATIC
+    for d in (0, 4, 12, 100, 136):
+        assert _packed(ctypes.byref(h), D=d) == UNSUP, d
+    assert _packed(ctypes.byref(h), H=0) == SHAPE
+    assert _packed(ctypes.byref(h), T=-1) == SHAPE
+    assert _packed(ctypes.byref(h), T=1 << 27, H=1) == SHAPE          # 16 output chunks per row exceed 2^31
+    assert _packed(ctypes.byref(h), qkv=None) == NULL
+    assert _packed(ctypes.byref(h), qkv=MISALIGNED) == ALIGN
+    for i in range(3):
+        o = [FAKE] * 3
+        o[i] = None
+        assert _packed(ctypes.byref(h), outs=tuple(o)) == NULL
+        o[i] = MISALIGNED
+        assert _packed(ctypes.byref(h), outs=tuple(o)) == ALIGN
 
 
 def _battn(q=FAKE, k=FAKE, v=FAKE, cu=FAKE, B=1, T=8, H=2, D=128, out=FAKE):

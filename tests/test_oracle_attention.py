@@ -238,3 +238,23 @@ def test_float_attention_matches_code_attention_on_decoded_values():
     a = oracle.attention(*codes, descale, _cu(seqlens))
     f = oracle.attention_float(*(oracle.decode(c) * float(d) for c, d in zip(codes, descale)), _cu(seqlens))
     assert np.array_equal(a, f)
+
+
+def test_head_dim_80_lossless_equals_torch_sdpa():
+    """Codes zero-padded to 128 dims, attention over the first 80: the scale is 1/sqrt(80) (library SDPA on the
+    decoded values, which quantization reproduces exactly because every value is an E4M3 value times 2^-6)."""
+    rng = np.random.default_rng(41)
+    seqlens = [5, 33]
+    T, H, D = sum(seqlens), 2, 80
+    vals = decode(np.arange(256, dtype=np.uint8))
+    vals = vals[np.isfinite(vals) & (np.abs(vals) <= 7.0)]
+    xs = []
+    for _ in range(3):
+        x = rng.choice(vals, size=(T, H, D)).astype(np.float64) * 2.0 ** -6
+        x[0, 0, 0] = 7.0 * 2.0 ** -6             # amax exactly 7 * 2^-6: scales are powers of two
+        xs.append(x)
+    st = ScaleState()
+    q8, k8, v8, descale, _ = quantize_qkv(st, "dynamic", *(x.astype(np.float32) for x in xs))
+    got = attention(q8, k8, v8, descale, _cu(seqlens))
+    ref = _sdpa64(*xs, _cu(seqlens))
+    assert np.allclose(got, ref, rtol=0, atol=1e-12)

@@ -64,3 +64,30 @@ def test_zero_tensor_quantizes_to_zero():
     q8, k8, v8, descale, _ = quantize_qkv(st, "dynamic", z, z, -z)
     assert np.all(q8 == 0) and np.all(k8 == 0) and np.all(v8 == 0x80)
     assert np.all(np.isfinite(descale)) and np.all(descale > 0)
+
+
+def test_packed_quantize_brute_force():
+    """Fused [T, 3, H, D] input: element by element, each code is encode(fp32(x * inv)) of its own tensor's
+    scale at [t, h, d], dims past D are 0, and the amax counts only the tensor's own real elements."""
+    from oracle import ScaleState, encode, quantize_qkv_packed
+
+    rng = np.random.default_rng(12)
+    T, H, D = 3, 2, 16
+    qkv = rng.standard_normal((T, 3, H, D)).astype(np.float32) * np.array([1.0, 7.0, 0.25], np.float32)[None, :, None, None]
+    qkv = qkv.astype(np.float32)
+    q8, k8, v8, descale, observed = quantize_qkv_packed(ScaleState(), "dynamic", qkv)
+    codes = (q8, k8, v8)
+    for which in range(3):
+        brute_amax = 0.0
+        for t in range(T):
+            for h in range(H):
+                for d in range(D):
+                    brute_amax = max(brute_amax, abs(float(qkv[t, which, h, d])))
+        assert observed[which] == np.float32(brute_amax)
+        inv = np.float32(448.0) / np.float32(max(brute_amax, 2.0 ** -100))
+        for t in range(T):
+            for h in range(H):
+                for d in range(128):
+                    want = 0 if d >= D else int(encode(np.array([np.float32(qkv[t, which, h, d]) * inv], np.float32))[0])
+                    assert codes[which][t, h, d] == want, (which, t, h, d)
+    assert descale.dtype == np.float32 and descale.shape == (3,)
