@@ -27,24 +27,12 @@ namespace {
 
 using namespace attn;
 
-constexpr int kRow = 2 * kD;              // bytes per bf16 row (one head of one token)
-constexpr int kTileBytes = kBN * kRow;    // 32 KiB per K or V tile
 constexpr int kLdsK = 0;
 constexpr int kLdsV = 2 * kTileBytes;
 constexpr int kLdsBytes = 4 * kTileBytes;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
-// LDS layouts: [key][128] bf16 rows of 256 B (16 chunks of 16 B); logical
-// chunk c of row r sits at chunk c ^ swz(r).
-//   K (A operand of S = K Q^T, ds_read_b128): 16 lanes read rows r..r+15 of
-//     one logical chunk; swz_k(r) = r & 15 spreads them over all 16 chunk
-//     positions (all 64 banks).
-//   V (V^T operand, ds_read_b64_tr_b16): 32 lanes read 8-byte pieces of
-//     rows {4g + e : g in 0..1, e in 0..3} (+ a multiple of 16), a 32-byte
-//     span per row; swz_v(r) = (r & 7) << 1 moves the span of row r to
-//     32 * (span ^ (r & 7)), 8 distinct spans covering all banks.
-__device__ inline uint32_t swz_k(uint32_t r) { return r & 15; }
-__device__ inline uint32_t swz_v(uint32_t r) { return (r & 7) << 1; }
+// LDS layouts: the K and V tiles of attn_common.h (swz_k, swz_v).
 
 // Asynchronous fetch of one 128-key tile of K or V: wave w fills the 1 KiB
 // segments 4w .. 4w + 3 (tile rows [16w, 16w + 16)); lane l of a segment
@@ -92,88 +80,13 @@ struct Wave {
     __device__ __forceinline__ void load_v(lds_u8* lds, int t, int buf) const {
         issue_tile_load(v, row_stride, h, seq_lo + t * kBN, seq_hi, lds + kLdsV + buf * kTileBytes, wave, g_v);
     }
-    // V^T operand of O^T += V^T P^T for d block db and 32-key chunk j.
-    // Transpose read: in each 16-lane group, lane r receives element e from
-    // the address of lane 4e + (r >> 2), offset r & 3.  Lane 4e + c of group
-    // g points at key 32j + 16hh + 4g + e, dims 16db + 4c .. 16db + 4c + 3,
-    // so lane r gets keys 32j + 16hh + 4g + e (e = 0..3) of dim 16db + r: the
-    // key order of the P^T operand.
-    __device__ __forceinline__ bf16x8 read_v(const unsigned char* vbase, int db, int j) const {
-        const unsigned char* base = vbase + (v_rd ^ (uint32_t)(db << 5)) + j * 32 * kRow;
-        typedef short v4s __attribute__((ext_vector_type(4)));
-        const v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(lds_u8*)base);
-        const v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4s*)(lds_u8*)(base + 16 * kRow));
-        const bf16x4 x = __builtin_bit_cast(bf16x4, a), y = __builtin_bit_cast(bf16x4, b);
-        return bf16x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-    }
 };
-
-// S = K Q^T for one key tile: s[kb][qb] holds keys 16kb + 4g + i of query r16.
-// The K operands of block kb + 1 are requested before the MFMAs of block kb
-// issue (the scheduling fence keeps them there), so LDS latency overlaps
-// the matrix work.
-__device__ __forceinline__ void qk_phase(const Wave& w, const unsigned char* smem, int buf, v4f (&s)[8][kQB]) {
-    const unsigned char* kbase = smem + kLdsK + buf * kTileBytes;
-    bf16x8 kop[2][4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) kop[0][c] = *(const bf16x8*)(kbase + (w.k_rd ^ (uint32_t)(c << 4)));
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb) {
-        if (kb + 1 < 8) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-                kop[(kb + 1) & 1][c] = *(const bf16x8*)(kbase + (w.k_rd ^ (uint32_t)(c << 4)) + (kb + 1) * 16 * kRow);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) s[kb][qb] = v4f{0, 0, 0, 0};
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-            for (int qb = 0; qb < kQB; ++qb) s[kb][qb] = mfma_bf16(kop[kb & 1][c], w.q[qb][c], s[kb][qb]);
-    }
-}
 
 // The softmax step of a key tile is split over two slots to even out the
 // VALU work of the two groups: softmax_head (mask, row max, rescale, and p
 // of key blocks [0, kSplit)) and, in the next slot, the remaining key
 // blocks followed by the P^T operands.
 constexpr int kSplit = 5;
-
-// P^T operands: pop[qb][j] holds p of keys 32j + 4g + i (elements 0..3) and
-// 32j + 16 + 4g + i (elements 4..7) of query r16, rounded to bf16; l
-// accumulates the fp32 p.
-__device__ __forceinline__ void pack_phase(const Wave& w, v4f (&p)[8][kQB], int nk, bf16x8 (&pop)[kQB][4],
-                                           float (&l)[kQB]) {
-    exp_blocks<kSplit, 8>(w, p, nk);
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-        float sum = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const v4f a = p[2 * j][qb], b = p[2 * j + 1][qb];
-            pop[qb][j] = bf16x8{(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3],
-                                (__bf16)b[0], (__bf16)b[1], (__bf16)b[2], (__bf16)b[3]};
-            sum += ((a[0] + a[1]) + (a[2] + a[3])) + ((b[0] + b[1]) + (b[2] + b[3]));
-        }
-        l[qb] += sum;
-    }
-}
-
-// O^T += V^T P^T for one key tile.
-__device__ __forceinline__ void pv_phase(Wave& w, const unsigned char* smem, int buf, const bf16x8 (&pop)[kQB][4]) {
-    const unsigned char* vbase = smem + kLdsV + buf * kTileBytes;
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const bf16x8 vop = w.read_v(vbase, db, j);
-#pragma unroll
-            for (int qb = 0; qb < kQB; ++qb) w.o[db][qb] = mfma_bf16(vop, pop[qb][j], w.o[db][qb]);
-        }
-    }
-}
 
 // The key loop of one wave group.  Period t (t = 0..nt) has four slots
 // separated by workgroup barriers:
@@ -199,30 +112,30 @@ __device__ __forceinline__ void key_loop(Wave& w, unsigned char* smem) {
         // slot 1
         if (t + 1 < nt) w.load_k(lds, t + 1, prev);
         if constexpr (!kB) {
-            if (t < nt) qk_phase(w, smem, cur, s);
+            if (t < nt) qk_tile(smem + kLdsK + cur * kTileBytes, w.k_rd, w.q, s);
         } else {
-            if (t >= 1) pack_phase(w, s, nk_p, pop, w.l);
+            if (t >= 1) pack_tile<kSplit>(w, s, nk_p, pop, w.l);
         }
         __syncthreads();
         // slot 2
         if constexpr (!kB) {
             if (t < nt) softmax_head<kSplit>(w, s, nk_t);
         } else {
-            if (t >= 1) pv_phase(w, smem, prev, pop);
+            if (t >= 1) pv_tile(smem + kLdsV + prev * kTileBytes, w.v_rd, pop, w.o);
         }
         wait_async_loads();
         __syncthreads();
         // slot 3
         if (t + 1 < nt) w.load_v(lds, t + 1, prev);
         if constexpr (!kB) {
-            if (t < nt) pack_phase(w, s, nk_t, pop, w.l);
+            if (t < nt) pack_tile<kSplit>(w, s, nk_t, pop, w.l);
         } else {
-            if (t < nt) qk_phase(w, smem, cur, s);
+            if (t < nt) qk_tile(smem + kLdsK + cur * kTileBytes, w.k_rd, w.q, s);
         }
         __syncthreads();
         // slot 4
         if constexpr (!kB) {
-            if (t < nt) pv_phase(w, smem, cur, pop);
+            if (t < nt) pv_tile(smem + kLdsV + cur * kTileBytes, w.v_rd, pop, w.o);
         } else {
             if (t < nt) softmax_head<kSplit>(w, s, nk_t);
         }
@@ -260,11 +173,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_fwd_kernel(
     w.wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in an SGPR
     const bool group_b = w.wave >= kWaves / 2;          // wave-uniform
     {
-        // K operand: row 16kb + r16 (swizzle r16), logical chunk 4g + c.
-        w.k_rd = (uint32_t)(r16 * kRow + 16 * ((4 * g) ^ r16));
-        // V^T read: lane 4e + c of group g, row 4g + e (swizzle 4(g & 1) + e).
-        const uint32_t e = (uint32_t)r16 >> 2, c = (uint32_t)r16 & 3;
-        w.v_rd = (4 * g + e) * kRow + 8 * c + 32 * (4 * (g & 1) + e);
+        w.k_rd = k_operand_offset(r16, g);
+        w.v_rd = v_operand_offset(r16, g);
         // Async loads: lane covers row rr = lane >> 4 of each 4-row segment
         // and physical chunk pc = lane & 15; segment 4w + r holds tile rows
         // 16w + 4r + rr, whose swizzles are 4r + rr (K) and 2(4(r & 1) + rr) (V).

@@ -162,5 +162,111 @@ __device__ __forceinline__ void exp_phase(W& w, v4f (&s)[8][kQB], int nk) {
     softmax_head<8>(w, s, nk);
 }
 
+
+// ---- bf16 operand tiles in LDS (both kernels run QK^T and P V on bf16) ----
+//
+// A K or V tile is [128 keys][128 dims] bf16: rows of 256 B, 16 chunks of
+// 16 B; logical chunk c of row r sits at chunk c ^ swz(r).
+//   K (A operand of S = K Q^T, ds_read_b128): 16 lanes read rows r..r+15 of
+//     one logical chunk; swz_k(r) = r & 15 spreads them over all 16 chunk
+//     positions (all 64 banks).
+//   V (V^T operand, ds_read_b64_tr_b16): 32 lanes read 8-byte pieces of
+//     rows {4g + e : g in 0..1, e in 0..3} (+ a multiple of 16), a 32-byte
+//     span per row; swz_v(r) = (r & 7) << 1 moves the span of row r to
+//     32 * (span ^ (r & 7)), 8 distinct spans covering all banks.
+constexpr int kRow = 2 * kD;              // bytes per bf16 row (one head of one token)
+constexpr int kTileBytes = kBN * kRow;    // 32 KiB per K or V tile
+__device__ inline uint32_t swz_k(uint32_t r) { return r & 15; }
+__device__ inline uint32_t swz_v(uint32_t r) { return (r & 7) << 1; }
+
+// Lane offsets inside a tile for lane (r16, g).
+//   K operand: row r16, logical chunk 4g + c at k_rd ^ (c << 4) (+ 16 rows per key block).
+//   V^T transpose read: lane 4e + c of group g points at row 4g + e, dims
+//   4c .. 4c + 3 of a 16-dim block, i.e. byte 8c + 32 (4(g & 1) + e) after
+//   the swizzle; dim block db at v_rd ^ (db << 5).
+__device__ inline uint32_t k_operand_offset(int r16, int g) { return (uint32_t)(r16 * kRow + 16 * ((4 * g) ^ r16)); }
+__device__ inline uint32_t v_operand_offset(int r16, int g) {
+    const uint32_t e = (uint32_t)r16 >> 2, c = (uint32_t)r16 & 3;
+    return (4 * (uint32_t)g + e) * kRow + 8 * c + 32 * (4 * ((uint32_t)g & 1) + e);
+}
+
+// S = K Q^T for one key tile: s[kb][qb] holds keys 16kb + 4g + i of query r16.
+// The K operands of block kb + 1 are requested before the MFMAs of block kb
+// issue (the scheduling fence keeps them there), so LDS latency overlaps
+// the matrix work.
+__device__ __forceinline__ void qk_tile(const unsigned char* kbase, uint32_t k_rd, const bf16x8 (&q)[kQB][4],
+                                        v4f (&s)[8][kQB]) {
+    bf16x8 kop[2][4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) kop[0][c] = *(const bf16x8*)(kbase + (k_rd ^ (uint32_t)(c << 4)));
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+        if (kb + 1 < 8) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                kop[(kb + 1) & 1][c] = *(const bf16x8*)(kbase + (k_rd ^ (uint32_t)(c << 4)) + (kb + 1) * 16 * kRow);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) s[kb][qb] = v4f{0, 0, 0, 0};
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int qb = 0; qb < kQB; ++qb) s[kb][qb] = mfma_bf16(kop[kb & 1][c], q[qb][c], s[kb][qb]);
+    }
+}
+
+// p of key blocks [kSplit, 8) (the rest of the softmax step), then the P^T
+// operands: pop[qb][j] holds p of keys 32j + 4g + i (elements 0..3) and
+// 32j + 16 + 4g + i (elements 4..7) of query r16, rounded to bf16; l
+// accumulates the fp32 p.
+template <int kSplit, class W>
+__device__ __forceinline__ void pack_tile(const W& w, v4f (&p)[8][kQB], int nk, bf16x8 (&pop)[kQB][4],
+                                          float (&l)[kQB]) {
+    exp_blocks<kSplit, 8>(w, p, nk);
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const v4f a = p[2 * j][qb], b = p[2 * j + 1][qb];
+            pop[qb][j] = bf16x8{(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3],
+                                (__bf16)b[0], (__bf16)b[1], (__bf16)b[2], (__bf16)b[3]};
+            sum += ((a[0] + a[1]) + (a[2] + a[3])) + ((b[0] + b[1]) + (b[2] + b[3]));
+        }
+        l[qb] += sum;
+    }
+}
+
+// V^T operand of O^T += V^T P^T for d block db and 32-key chunk j.
+// Transpose read: in each 16-lane group, lane r receives element e from the
+// address of lane 4e + (r >> 2), offset r & 3.  Lane 4e + c of group g
+// points at key 32j + 16hh + 4g + e, dims 16db + 4c .. 16db + 4c + 3, so lane
+// r gets keys 32j + 16hh + 4g + e (e = 0..3) of dim 16db + r: the key order
+// of the P^T operand.
+__device__ __forceinline__ bf16x8 read_vt(const unsigned char* vbase, uint32_t v_rd, int db, int j) {
+    const unsigned char* base = vbase + (v_rd ^ (uint32_t)(db << 5)) + j * 32 * kRow;
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    const v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(lds_u8*)base);
+    const v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4s*)(lds_u8*)(base + 16 * kRow));
+    const bf16x4 x = __builtin_bit_cast(bf16x4, a), y = __builtin_bit_cast(bf16x4, b);
+    return bf16x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+}
+
+// O^T += V^T P^T for one key tile.
+__device__ __forceinline__ void pv_tile(const unsigned char* vbase, uint32_t v_rd, const bf16x8 (&pop)[kQB][4],
+                                        v4f (&o)[8][kQB]) {
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bf16x8 vop = read_vt(vbase, v_rd, db, j);
+#pragma unroll
+            for (int qb = 0; qb < kQB; ++qb) o[db][qb] = mfma_bf16(vop, pop[qb][j], o[db][qb]);
+        }
+    }
+}
+
 }  // namespace attn
 }  // namespace qfa
