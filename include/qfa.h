@@ -167,8 +167,9 @@ const float* qfa_descale_ptr(const qfa_scale_state* st);
  *                  cu[num_seqs] = total_tokens; empty sequences are allowed
  *   head_dim       8..128 in steps of 8 (128 for qfa_quantize_qkv's codes)
  *   out            device bf16 [total_tokens, num_heads, head_dim] (out)
- * total_tokens must be below 2^31.  The kernel uses E4M3 probabilities split
- * into two terms (hi + lo) for the P*V product and float32 accumulation.
+ * total_tokens must be below 2^31.  The kernel converts the codes exactly to
+ * bf16 and runs both products on bf16 MFMAs with float32 accumulation; the
+ * probabilities are rounded to bf16 for the P*V product.
  */
 qfa_status qfa_fp8_varlen_attn(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                                const float* scales, const int32_t* cu_seqlens, int num_seqs,
