@@ -8,6 +8,11 @@ already resident in HBM when the timed region starts; the step rotates over
 several input sets whose total exceeds the 256 MB Infinity Cache, so each
 step's bf16 reads come from HBM.
 
+Before the W untimed warm-up steps, the step runs for --prewarm-s seconds
+(0.2 by default): the GPU needs about a tenth of a second of load to reach
+its steady clock, and steps timed before that run up to 7 % slower.  Then
+exactly K steps are timed.
+
 Prints ONE JSON line.  Work convention: 4 * sum(n_b^2) * H * 128 flop
 (two matmuls, 2 flop per multiply-add; softmax and the lo-term MFMAs not
 counted).  Peaks: dense FP8 MFMA 5000 TFLOP/s, dense BF16 MFMA 2500 TFLOP/s,
@@ -35,6 +40,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--prewarm-s", type=float, default=0.2,
+                   help="seconds of untimed steps before the warm-up steps (brings the GPU to its steady clock)")
     p.add_argument("--workload", type=int, default=3)
     p.add_argument("--sets", type=int, default=4, help="input sets rotated through (defeats the 256 MB cache)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -45,10 +52,91 @@ def parse():
     p.add_argument("--graph-overhead", action="store_true",
                    help="instead of the benchmark, compare eager launches with HIP-graph replay of the whole "
                         "path on the small workloads (1x256 tokens x 2 heads, 1x2304 tokens x 16 heads)")
+    p.add_argument("--all-configs", action="store_true",
+                   help="instead of the benchmark, time every workload (quantize in its own mode, FP8 attention, the "
+                        "BF16 baseline); one JSON line per workload")
     p.add_argument("--packed-head-dim", type=int, default=0,
                    help="instead of the benchmark, time the fused-QKV path at this head dim (8..128, step 8): "
                         "quantize from [T, 3, H, D] to padded codes, then FP8 attention writing [T, H, D]")
     return p.parse_args()
+
+
+def prewarm(fn, seconds):
+    """Run fn() (untimed) until `seconds` of wall time have passed, synchronising every few calls."""
+    import torch
+
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        fn(i)
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return i
+
+
+def all_configs(steps, warmup, prewarm_s):
+    """Per-workload times of the path's parts; each loop rotates over several input sets and starts after a short
+    untimed run of its own (a kernel's first launches in a process, and the GPU's clock ramp, run slow)."""
+    import torch
+
+    import quantized_flash_attn_amd as qfa
+    from workloads import WORKLOADS, cu_seqlens_tensor, make_qkv
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn, n):
+        prewarm(fn, prewarm_s)
+        for i in range(warmup):
+            fn(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    for wi, w in sorted(WORKLOADS.items()):
+        H, T = w.num_heads, w.total_tokens
+        n_sets = 4 if T <= 10000 else 2
+        sets = [make_qkv(w, f, device=dev) for f in range(n_sets)]
+        codes = [tuple(torch.empty((T, H, 128), dtype=torch.uint8, device=dev) for _ in range(3)) for _ in range(n_sets)]
+        out = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
+        cu = cu_seqlens_tensor(w.seqlens, dev)
+        mode = w.modes[0]
+        if mode == "static":
+            st = qfa.init_scale_state(dev, static_amax=[float(x.abs().max()) for x in sets[0]], margin=1.5)
+        else:
+            st = qfa.init_scale_state(dev)
+        # codes and scales of every set, for the attention-only loop
+        scs = []
+        for j in range(n_sets):
+            qfa.quantize_qkv(st, mode, *sets[j], *codes[j])
+            scs.append(qfa.descale(st).clone())
+        n = max(3, steps if T <= 10000 else steps // 4)
+        ms_q = timed(lambda i: qfa.quantize_qkv(st, mode, *sets[i % n_sets], *codes[i % n_sets]), n)
+        ms_a = timed(lambda i: qfa.fp8_varlen_attn(*codes[i % n_sets], scs[i % n_sets], cu, H, out=out), n)
+        ms_b = timed(lambda i: qfa.bf16_varlen_attn(*sets[i % n_sets], cu, H, out=out), n)
+        qbytes = (5 if mode == "dynamic" else 3) * 3 * T * H * 128
+        flop = w.attn_flop
+        print(json.dumps({"config": {
+            "workload": w.name, "seqlens": list(w.seqlens), "num_heads": H, "scaling_mode": mode,
+            "input_sets": n_sets,
+            "quantize": {"ms": round(ms_q, 4), "gbs": round(qbytes / (ms_q * 1e-3) / 1e9, 1),
+                         "frac_hbm_peak": round(qbytes / (ms_q * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+            "fp8_attention": {"ms": round(ms_a, 4), "tflops": round(flop / (ms_a * 1e-3) / 1e12, 1),
+                              "frac_fp8_peak": round(flop / (ms_a * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4)},
+            "step_incl_quant": {"ms": round(ms_q + ms_a, 4), "tflops": round(flop / ((ms_q + ms_a) * 1e-3) / 1e12, 1)},
+            "bf16_attention": {"ms": round(ms_b, 4), "tflops": round(flop / (ms_b * 1e-3) / 1e12, 1)},
+            "fp8_speedup_incl_quant": round(ms_b / (ms_q + ms_a), 3),
+            "launches": n}}), flush=True)
+        del sets, codes, out
+        torch.cuda.empty_cache()
 
 
 def packed_path(head_dim, steps, warmup):
@@ -272,6 +360,9 @@ def main():
     if args.graph_overhead:
         graph_overhead(args.steps)
         return
+    if args.all_configs:
+        all_configs(args.steps, args.warmup, args.prewarm_s)
+        return
     if args.packed_head_dim:
         packed_path(args.packed_head_dim, args.steps, args.warmup)
         return
@@ -303,7 +394,9 @@ def main():
         qfa.quantize_qkv(st, "dynamic", q, k, v, q8, k8, v8)
         qfa.fp8_varlen_attn(q8, k8, v8, scales, cu, H, out=out)
 
-    def timed(fn, n):
+    def timed(fn, n, warm_s=0.0):
+        if warm_s > 0:
+            prewarm(fn, warm_s)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record(stream)
@@ -313,6 +406,7 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n  # ms
 
+    prewarm(step, args.prewarm_s)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -322,10 +416,11 @@ def main():
     ms_step = ms_step_ev
 
     # component timings on the same stream
-    ms_attn = timed(lambda i: qfa.fp8_varlen_attn(q8, k8, v8, scales, cu, H, out=out), args.steps)
-    ms_quant = timed(lambda i: qfa.quantize_qkv(st, "dynamic", *sets[i % len(sets)], q8, k8, v8), args.steps)
+    # component loops, each after a short untimed run of its own (a kernel's first launches in a process run slow)
+    ms_attn = timed(lambda i: qfa.fp8_varlen_attn(q8, k8, v8, scales, cu, H, out=out), args.steps, 0.05)
+    ms_quant = timed(lambda i: qfa.quantize_qkv(st, "dynamic", *sets[i % len(sets)], q8, k8, v8), args.steps, 0.05)
     # the BF16 baseline on the same inputs (the pages state FP8 gains as BF16 -> FP8 pairs)
-    ms_bf16 = timed(lambda i: qfa.bf16_varlen_attn(*sets[i % len(sets)], cu, H, out=out), args.steps)
+    ms_bf16 = timed(lambda i: qfa.bf16_varlen_attn(*sets[i % len(sets)], cu, H, out=out), args.steps, 0.1)
 
     flop = w.attn_flop
     value = flop / (ms_step * 1e-3) / 1e12
