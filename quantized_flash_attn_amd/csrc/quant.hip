@@ -11,7 +11,11 @@
 // Kernels (both HBM-streaming):
 //   amax_partial_kernel    grid (P, 3): max of |x| as bf16 bit patterns,
 //                          one partial per workgroup, no atomics; workgroup
-//                          (0, 0) also snapshots the ring cursor
+//                          (0, 0) also snapshots the ring cursor.  Its loads
+//                          allocate in the caches (unlike quantize's
+//                          streaming loads), so that quantize, which reads
+//                          the same tensors right after, finds part of them
+//                          in the 256 MB Infinity Cache.
 //   quantize_kernel        grid (G, 3): x * inv -> clamp +-448 -> E4M3 (RNE).
 //                          Dynamic mode: every workgroup first reduces its
 //                          tensor's partials and derives the forward's scale
@@ -99,16 +103,16 @@ __global__ __launch_bounds__(kThreads) void amax_partial_kernel(const u32x4* __r
     int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     uint32_t m = 0;
     for (; i + 3 * stride < n_chunks; i += 4 * stride) {
-        const u32x4 a = __builtin_nontemporal_load(src + i);
-        const u32x4 b = __builtin_nontemporal_load(src + i + stride);
-        const u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
-        const u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
+        const u32x4 a = src[i];
+        const u32x4 b = src[i + stride];
+        const u32x4 c = src[i + 2 * stride];
+        const u32x4 d = src[i + 3 * stride];
         m = max_abs_bits(a, m);
         m = max_abs_bits(b, m);
         m = max_abs_bits(c, m);
         m = max_abs_bits(d, m);
     }
-    for (; i < n_chunks; i += stride) m = max_abs_bits(__builtin_nontemporal_load(src + i), m);
+    for (; i < n_chunks; i += stride) m = max_abs_bits(src[i], m);
     m = wave_max_u32(m);
     __shared__ uint32_t red[kThreads / 64];
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
@@ -256,16 +260,16 @@ __global__ __launch_bounds__(kThreads) void amax_packed_kernel(const u32x4* __re
     uint32_t i = blockIdx.x * kThreads + threadIdx.x;
     // four independent loads in flight per thread (i + 3 stride < n_chunks < 2^31: no overflow)
     for (; i + 3 * stride < n_chunks; i += 4 * stride) {
-        const u32x4 a = __builtin_nontemporal_load(src(i));
-        const u32x4 b = __builtin_nontemporal_load(src(i + stride));
-        const u32x4 c = __builtin_nontemporal_load(src(i + 2 * stride));
-        const u32x4 d = __builtin_nontemporal_load(src(i + 3 * stride));
+        const u32x4 a = *src(i);
+        const u32x4 b = *src(i + stride);
+        const u32x4 c = *src(i + 2 * stride);
+        const u32x4 d = *src(i + 3 * stride);
         m = max_abs_bits(a, m);
         m = max_abs_bits(b, m);
         m = max_abs_bits(c, m);
         m = max_abs_bits(d, m);
     }
-    for (; i < n_chunks; i += stride) m = max_abs_bits(__builtin_nontemporal_load(src(i)), m);
+    for (; i < n_chunks; i += stride) m = max_abs_bits(*src(i), m);
     m = wave_max_u32(m);
     __shared__ uint32_t red[kThreads / 64];
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
