@@ -54,7 +54,10 @@
 //                   layout, rounded to bf16.  Two E4M3 terms of p (hi + lo)
 //                   on the fp8 MFMA would cost the same matrix time plus two
 //                   slow conversions per pair of p; one E4M3 term is too
-//                   coarse.  l sums the fp32 p.
+//                   coarse.  l is the row sum of the same bf16 p, taken by an
+//                   MFMA with an all-ones A operand (8 per tile, in the
+//                   LDS-bound P V slot, instead of 64 fp32 adds in the VALU
+//                   slot), so O / l is a convex combination of V rows.
 //   epilogue        out = bf16(O * s_v / l).
 
 #include <cmath>
@@ -136,6 +139,30 @@ __device__ __forceinline__ void convert_tile(const unsigned char* src, unsigned 
     }
 }
 
+// P^T operands from p (see pack_tile, without the fp32 row sum).
+__device__ __forceinline__ void pack_bf16(const v4f (&p)[8][kQB], bf16x8 (&pop)[kQB][4]) {
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const v4f a = p[2 * j][qb], b = p[2 * j + 1][qb];
+            pop[qb][j] = bf16x8{(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3],
+                                (__bf16)b[0], (__bf16)b[1], (__bf16)b[2], (__bf16)b[3]};
+        }
+}
+
+// l += the tile's row sums of the bf16 p: with every A entry 1, each output
+// entry of a 16x16x32 product is the sum of its query's 32 p, already
+// reduced over the lanes.
+__device__ __forceinline__ void row_sums(const bf16x8 (&pop)[kQB][4], v4f (&l)[kQB]) {
+    const __bf16 one = (__bf16)1.0f;
+    const bf16x8 ones = {one, one, one, one, one, one, one, one};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) l[qb] = mfma_bf16(ones, pop[qb][j], l[qb]);
+}
+
 // Everything one wave carries through the key loop.  Lane (r16, g) of a
 // 16x16 accumulator holds rows 4g..4g+3 of column r16; every score and
 // output block uses that layout (scores: rows = keys, columns = queries;
@@ -153,7 +180,7 @@ struct Wave {
     bf16x8 q[kQB][4];      // Q operand (B of S = K Q^T)
     float m[kQB];          // running row max of the raw scores (lags by <= slack / c)
     v4f o[8][kQB];         // O^T blocks [d block][query block]
-    float l[kQB];          // running sum of p over the keys this lane holds (reduced over the quad at the end)
+    v4f l[kQB];            // running row sums of the bf16 p per query (the 4 entries are equal)
 
     __device__ __forceinline__ void load_k8(lds_u8* lds, int t) const {
         issue_code_tile_load(k8, row_stride, h, seq_lo + t * kBN, seq_hi, lds + kLdsK8, wave, g_ld);
@@ -194,7 +221,10 @@ __device__ __forceinline__ void key_loop(Wave& w, unsigned char* smem) {
         if constexpr (!kB) {
             if (t < nt) qk_tile(smem + kLdsK + cur * kTileBytes, w.k_rd, w.q, s);
         } else {
-            if (t >= 1) pack_tile<kSplit>(w, s, nk_p, pop, w.l);
+            if (t >= 1) {
+                exp_blocks<kSplit, 8>(w, s, nk_p);
+                pack_bf16(s, pop);
+            }
             if (t >= 1 && t < nt) w.convert_v(smem, cur);
         }
         __syncthreads();
@@ -202,14 +232,20 @@ __device__ __forceinline__ void key_loop(Wave& w, unsigned char* smem) {
         if constexpr (!kB) {
             if (t < nt) softmax_head<kSplit>(w, s, nk_t);
         } else {
-            if (t >= 1) pv_tile(smem + kLdsV + prev * kTileBytes, w.v_rd, pop, w.o);
+            if (t >= 1) {
+                pv_tile(smem + kLdsV + prev * kTileBytes, w.v_rd, pop, w.o);
+                row_sums(pop, w.l);
+            }
         }
         wait_async_loads();
         __syncthreads();
         // slot 3
         if (t + 1 < nt) w.load_v8(lds, t + 1);
         if constexpr (!kB) {
-            if (t < nt) pack_tile<kSplit>(w, s, nk_t, pop, w.l);
+            if (t < nt) {
+                exp_blocks<kSplit, 8>(w, s, nk_t);
+                pack_bf16(s, pop);
+            }
             if (t + 1 < nt) w.convert_k(smem, prev);
         } else {
             if (t < nt) qk_tile(smem + kLdsK + cur * kTileBytes, w.k_rd, w.q, s);
@@ -217,7 +253,10 @@ __device__ __forceinline__ void key_loop(Wave& w, unsigned char* smem) {
         __syncthreads();
         // slot 4
         if constexpr (!kB) {
-            if (t < nt) pv_tile(smem + kLdsV + cur * kTileBytes, w.v_rd, pop, w.o);
+            if (t < nt) {
+                pv_tile(smem + kLdsV + cur * kTileBytes, w.v_rd, pop, w.o);
+                row_sums(pop, w.l);
+            }
         } else {
             if (t < nt) softmax_head<kSplit>(w, s, nk_t);
         }
@@ -290,7 +329,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     for (int qb = 0; qb < kQB; ++qb) {
 #pragma unroll
         for (int db = 0; db < 8; ++db) w.o[db][qb] = v4f{0, 0, 0, 0};
-        w.l[qb] = 0.0f;
+        w.l[qb] = v4f{0, 0, 0, 0};
         w.m[qb] = kMInit;
     }
 
@@ -318,7 +357,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     for (int qb = 0; qb < kQB; ++qb) {
         const int qi = q0 + w.wave * (16 * kQB) + qb * 16 + r16;
         if (qi < seq_hi) {
-            const float f = s_v / quad_sum(w.l[qb]);
+            const float f = s_v / w.l[qb][0];
             __bf16* dst = out + ((size_t)qi * num_heads + h) * head_dim + 4 * g;
 #pragma unroll
             for (int db = 0; db < 8; ++db) {
