@@ -8,9 +8,11 @@
 // Inputs are E4M3 codes in HBM (1 byte per element); the kernel works on the
 // code values and folds the per-tensor scales into the softmax and epilogue.
 // Code rows are always 128 dims wide: a head_dim D below 128 arrives
-// zero-padded (the zeros add nothing to Q K^T and give zero output dims),
-// the softmax scale is 1/sqrt(D), and only the D real output dims are
-// written, to rows D wide.
+// zero-padded.  The kernel is instantiated for the number of 32-dim chunks
+// (kDC) and 16-dim output blocks (kDB) that cover D, so the padding beyond
+// them costs no matrix work (D = 80 or 72: 3 chunks, 5 blocks); the rest of
+// the padding adds nothing to Q K^T.  The softmax scale is 1/sqrt(D), and
+// only the D real output dims are written, to rows D wide.
 //
 // Work decomposition
 //   * One workgroup = 8 waves = one (head, 256-query tile of one sequence);
@@ -166,8 +168,11 @@ __device__ __forceinline__ void row_sums(const bf16x8 (&pop)[kQB][4], v4f (&l)[k
 // Everything one wave carries through the key loop.  Lane (r16, g) of a
 // 16x16 accumulator holds rows 4g..4g+3 of column r16; every score and
 // output block uses that layout (scores: rows = keys, columns = queries;
-// output: rows = head dims, columns = queries).
+// output: rows = head dims, columns = queries).  kDB_: live 16-dim output
+// blocks (o[db] for db >= kDB_ is never touched).
+template <int kDB_>
 struct Wave {
+    static constexpr int kDB = kDB_;
     const uint8_t* k8;
     const uint8_t* v8;
     uint32_t row_stride;   // bytes between tokens of one head (uniform)
@@ -206,8 +211,8 @@ struct Wave {
 // V_t is read in slot 4 of period t (A) and slot 2 of period t+1 (B), and
 // rewritten with V_{t+2} at slot 1 of period t+2; each staging buffer is
 // converted before the next load into it is issued.
-template <bool kB>
-__device__ __forceinline__ void key_loop(Wave& w, unsigned char* smem) {
+template <bool kB, int kDC, int kDB>
+__device__ __forceinline__ void key_loop(Wave<kDB>& w, unsigned char* smem) {
     lds_u8* const lds = (lds_u8*)smem;
     const int nt = w.nt;
     v4f s[8][kQB];
@@ -219,7 +224,7 @@ __device__ __forceinline__ void key_loop(Wave& w, unsigned char* smem) {
         // slot 1
         if (t + 1 < nt) w.load_k8(lds, t + 1);
         if constexpr (!kB) {
-            if (t < nt) qk_tile(smem + kLdsK + cur * kTileBytes, w.k_rd, w.q, s);
+            if (t < nt) qk_tile<kDC>(smem + kLdsK + cur * kTileBytes, w.k_rd, w.q, s);
         } else {
             if (t >= 1) {
                 exp_blocks<kSplit, 8>(w, s, nk_p);
@@ -233,7 +238,7 @@ __device__ __forceinline__ void key_loop(Wave& w, unsigned char* smem) {
             if (t < nt) softmax_head<kSplit>(w, s, nk_t);
         } else {
             if (t >= 1) {
-                pv_tile(smem + kLdsV + prev * kTileBytes, w.v_rd, pop, w.o);
+                pv_tile<kDB>(smem + kLdsV + prev * kTileBytes, w.v_rd, pop, w.o);
                 row_sums(pop, w.l);
             }
         }
@@ -248,13 +253,13 @@ __device__ __forceinline__ void key_loop(Wave& w, unsigned char* smem) {
             }
             if (t + 1 < nt) w.convert_k(smem, prev);
         } else {
-            if (t < nt) qk_tile(smem + kLdsK + cur * kTileBytes, w.k_rd, w.q, s);
+            if (t < nt) qk_tile<kDC>(smem + kLdsK + cur * kTileBytes, w.k_rd, w.q, s);
         }
         __syncthreads();
         // slot 4
         if constexpr (!kB) {
             if (t < nt) {
-                pv_tile(smem + kLdsV + cur * kTileBytes, w.v_rd, pop, w.o);
+                pv_tile<kDB>(smem + kLdsV + cur * kTileBytes, w.v_rd, pop, w.o);
                 row_sums(pop, w.l);
             }
         } else {
@@ -265,6 +270,7 @@ __device__ __forceinline__ void key_loop(Wave& w, unsigned char* smem) {
     }
 }
 
+template <int kDC, int kDB>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8, const uint8_t* __restrict__ v8,
     const float* __restrict__ scales, const int32_t* __restrict__ cu, int num_seqs, int num_heads,
@@ -283,7 +289,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     const int q0 = seq_lo + (vt - (seq_lo / kBM + b)) * kBM;
     if (q0 >= seq_hi) return;  // spare tile (uniform over the workgroup)
 
-    Wave w;
+    Wave<kDB> w;
     w.k8 = k8;
     w.v8 = v8;
     w.row_stride = (uint32_t)num_heads * kD;
@@ -306,29 +312,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     w.load_k8(lds, 0);
     w.load_v8(lds, 0);
 
-    // Q operand (B of S = K Q^T, bf16 16x16x32): lane holds query r16 of the
-    // block and the 32 head dims [32g, 32g + 32) as four 8-element chunks; the
-    // K operand uses the same (lane group, chunk, element) -> dim mapping.
+    // Q operand (B of S = K Q^T, bf16 16x16x32): for the c-th MFMA, lane
+    // holds query r16 of the block and head dims 32c + 8g .. + 7, the
+    // mapping the K operand uses.
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
         const int qi = q0 + w.wave * (16 * kQB) + qb * 16 + r16;
-        u32x4 a = {0, 0, 0, 0}, c = {0, 0, 0, 0};
-        if (qi < seq_hi) {
-            const u32x4* src = (const u32x4*)(q8 + (size_t)qi * w.row_stride + (size_t)h * kD + 32 * g);
-            a = src[0];
-            c = src[1];
+#pragma unroll
+        for (int c = 0; c < kDC; ++c) {
+            u32x2 a = {0, 0};
+            if (qi < seq_hi) a = *(const u32x2*)(q8 + (size_t)qi * w.row_stride + (size_t)h * kD + 32 * c + 8 * g);
+            w.q[qb][c] = codes_to_bf16x8(a[0], a[1]);
         }
-        w.q[qb][0] = codes_to_bf16x8(a[0], a[1]);
-        w.q[qb][1] = codes_to_bf16x8(a[2], a[3]);
-        w.q[qb][2] = codes_to_bf16x8(c[0], c[1]);
-        w.q[qb][3] = codes_to_bf16x8(c[2], c[3]);
     }
     const float s_q = scales[0], s_k = scales[1], s_v = scales[2];
     w.cexp = s_q * s_k * log2e_rsqrt_d;
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
 #pragma unroll
-        for (int db = 0; db < 8; ++db) w.o[db][qb] = v4f{0, 0, 0, 0};
+        for (int db = 0; db < kDB; ++db) w.o[db][qb] = v4f{0, 0, 0, 0};
         w.l[qb] = v4f{0, 0, 0, 0};
         w.m[qb] = kMInit;
     }
@@ -346,9 +348,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     // loop, so its registers are allocated for its own live ranges; both
     // copies execute the same sequence of barriers.
     if (group_b)
-        key_loop<true>(w, smem);
+        key_loop<true, kDC, kDB>(w, smem);
     else
-        key_loop<false>(w, smem);
+        key_loop<false, kDC, kDB>(w, smem);
 
     // ---- epilogue: lane holds O^T[d = 16db + 4g + i][query r16]; the output
     // rows hold head_dim dims (a multiple of 8, so a lane's 4 dims are all
@@ -360,7 +362,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
             const float f = s_v / w.l[qb][0];
             __bf16* dst = out + ((size_t)qi * num_heads + h) * head_dim + 4 * g;
 #pragma unroll
-            for (int db = 0; db < 8; ++db) {
+            for (int db = 0; db < kDB; ++db) {
                 if (16 * db + 4 * g < head_dim) {
                     bf16x4 r;
                     r[0] = (__bf16)(w.o[db][qb][0] * f);
@@ -386,8 +388,15 @@ hipError_t launch_attention(const uint8_t* q8, const uint8_t* k8, const uint8_t*
     // log2(e) / sqrt(head_dim) in float32: for head_dim 128 this is the
     // product of the two float32 constants.
     const float rsqrt_d = head_dim == kD ? kRsqrtD : (float)(1.0 / std::sqrt((double)head_dim));
-    attn_fwd_kernel<<<(unsigned)nwg, kThreads, 0, s>>>(q8, k8, v8, scales, cu_seqlens, num_seqs, num_heads,
-                                                       tph, head_dim, kLog2e * rsqrt_d, (__bf16*)out);
+    const float c = kLog2e * rsqrt_d;
+    // the smallest instantiation whose 32-dim chunks and 16-dim blocks cover head_dim
+    auto* kernel = attn_fwd_kernel<4, 8>;
+    if (head_dim <= 32) kernel = attn_fwd_kernel<1, 2>;
+    else if (head_dim <= 64) kernel = attn_fwd_kernel<2, 4>;
+    else if (head_dim <= 80) kernel = attn_fwd_kernel<3, 5>;
+    else if (head_dim <= 96) kernel = attn_fwd_kernel<3, 6>;
+    kernel<<<(unsigned)nwg, kThreads, 0, s>>>(q8, k8, v8, scales, cu_seqlens, num_seqs, num_heads, tph, head_dim, c,
+                                              (__bf16*)out);
     return hipGetLastError();
 }
 

@@ -60,6 +60,7 @@ __device__ inline void issue_tile_load(const unsigned char* __restrict__ src, ui
 // 16x16 accumulator holds rows 4g..4g+3 of column r16 (scores: rows = keys,
 // columns = queries; output: rows = head dims, columns = queries).
 struct Wave {
+    static constexpr int kDB = 8;   // live 16-dim output blocks
     const unsigned char* k;
     const unsigned char* v;
     uint32_t row_stride;   // bytes between tokens of one head (uniform)
@@ -192,18 +193,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_fwd_kernel(
     w.load_k(lds, 0, 0);
     w.load_v(lds, 0, 0);
 
-    // Q operand (B of S = K Q^T, bf16 16x16x32): lane holds query r16 of the
-    // block and the 32 head dims [32g, 32g + 32) as four 8-element chunks; the
-    // K operand uses the same (lane group, chunk, element) -> dim mapping.
+    // Q operand (B of S = K Q^T, bf16 16x16x32): for the c-th MFMA, lane
+    // holds query r16 of the block and head dims 32c + 8g .. + 7, the
+    // mapping the K operand uses.
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
         const int qi = q0 + w.wave * (16 * kQB) + qb * 16 + r16;
         u32x4 a[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
         if (qi < seq_hi) {
-            const u32x4* src = (const u32x4*)((const unsigned char*)q + (size_t)qi * w.row_stride + (size_t)h * kRow +
-                                              64 * g);
+            const unsigned char* src = (const unsigned char*)q + (size_t)qi * w.row_stride + (size_t)h * kRow + 16 * g;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) a[c] = src[c];
+            for (int c = 0; c < 4; ++c) a[c] = *(const u32x4*)(src + 64 * c);
         }
 #pragma unroll
         for (int c = 0; c < 4; ++c) w.q[qb][c] = __builtin_bit_cast(bf16x8, a[c]);

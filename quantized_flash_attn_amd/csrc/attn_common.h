@@ -17,6 +17,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -118,7 +119,7 @@ __device__ __forceinline__ void exp_blocks(const W& w, v4f (&s)[8][kQB], int nk)
 // scores of key blocks [0, kSplit) into p = 2^(S c + 8 - m c); the rest
 // follow with exp_blocks<kSplit, 8>.  s[kb][qb] holds keys 16kb + 4g + i of
 // query r16 (lane (r16, g), g4 = 4g).  W carries m[kQB], l[kQB],
-// o[8][kQB], cexp and g4.
+// o[8][kQB] (of which the first W::kDB dim blocks are live), cexp and g4.
 template <int kSplit, class W>
 __device__ __forceinline__ void softmax_head(W& w, v4f (&s)[8][kQB], int nk) {
     if (nk < kBN) {
@@ -150,7 +151,7 @@ __device__ __forceinline__ void softmax_head(W& w, v4f (&s)[8][kQB], int nk) {
             w.m[qb] = mn[qb];
             w.l[qb] *= alpha;
 #pragma unroll
-            for (int db = 0; db < 8; ++db) w.o[db][qb] *= alpha;
+            for (int db = 0; db < W::kDB; ++db) w.o[db][qb] *= alpha;
         }
     }
     exp_blocks<0, kSplit>(w, s, nk);
@@ -180,37 +181,41 @@ __device__ inline uint32_t swz_k(uint32_t r) { return r & 15; }
 __device__ inline uint32_t swz_v(uint32_t r) { return (r & 7) << 1; }
 
 // Lane offsets inside a tile for lane (r16, g).
-//   K operand: row r16, logical chunk 4g + c at k_rd ^ (c << 4) (+ 16 rows per key block).
+//   K operand of the c-th QK^T MFMA (dims [32c, 32c + 32), lane group g
+//   holding dims 32c + 8g .. + 7): row r16, logical chunk 4c + g, at
+//   k_rd ^ (c << 6) (+ 16 rows per key block).
 //   V^T transpose read: lane 4e + c of group g points at row 4g + e, dims
 //   4c .. 4c + 3 of a 16-dim block, i.e. byte 8c + 32 (4(g & 1) + e) after
 //   the swizzle; dim block db at v_rd ^ (db << 5).
-__device__ inline uint32_t k_operand_offset(int r16, int g) { return (uint32_t)(r16 * kRow + 16 * ((4 * g) ^ r16)); }
+__device__ inline uint32_t k_operand_offset(int r16, int g) { return (uint32_t)(r16 * kRow + 16 * (g ^ r16)); }
 __device__ inline uint32_t v_operand_offset(int r16, int g) {
     const uint32_t e = (uint32_t)r16 >> 2, c = (uint32_t)r16 & 3;
     return (4 * (uint32_t)g + e) * kRow + 8 * c + 32 * (4 * ((uint32_t)g & 1) + e);
 }
 
-// S = K Q^T for one key tile: s[kb][qb] holds keys 16kb + 4g + i of query r16.
-// The K operands of block kb + 1 are requested before the MFMAs of block kb
-// issue (the scheduling fence keeps them there), so LDS latency overlaps
-// the matrix work.
+// S = K Q^T for one key tile over the first kDC 32-dim chunks of the head
+// (the rest are zero padding when head_dim < 128): s[kb][qb] holds keys
+// 16kb + 4g + i of query r16.  The K operands of block kb + 1 are requested
+// before the MFMAs of block kb issue (the scheduling fence keeps them
+// there), so LDS latency overlaps the matrix work.
+template <int kDC = 4>
 __device__ __forceinline__ void qk_tile(const unsigned char* kbase, uint32_t k_rd, const bf16x8 (&q)[kQB][4],
                                         v4f (&s)[8][kQB]) {
     bf16x8 kop[2][4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) kop[0][c] = *(const bf16x8*)(kbase + (k_rd ^ (uint32_t)(c << 4)));
+    for (int c = 0; c < kDC; ++c) kop[0][c] = *(const bf16x8*)(kbase + (k_rd ^ (uint32_t)(c << 6)));
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
         if (kb + 1 < 8) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                kop[(kb + 1) & 1][c] = *(const bf16x8*)(kbase + (k_rd ^ (uint32_t)(c << 4)) + (kb + 1) * 16 * kRow);
+            for (int c = 0; c < kDC; ++c)
+                kop[(kb + 1) & 1][c] = *(const bf16x8*)(kbase + (k_rd ^ (uint32_t)(c << 6)) + (kb + 1) * 16 * kRow);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb) s[kb][qb] = v4f{0, 0, 0, 0};
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int c = 0; c < kDC; ++c)
 #pragma unroll
             for (int qb = 0; qb < kQB; ++qb) s[kb][qb] = mfma_bf16(kop[kb & 1][c], q[qb][c], s[kb][qb]);
     }
@@ -254,11 +259,12 @@ __device__ __forceinline__ bf16x8 read_vt(const unsigned char* vbase, uint32_t v
     return bf16x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
 }
 
-// O^T += V^T P^T for one key tile.
+// O^T += V^T P^T for one key tile, over the first kDB 16-dim blocks.
+template <int kDB = 8>
 __device__ __forceinline__ void pv_tile(const unsigned char* vbase, uint32_t v_rd, const bf16x8 (&pop)[kQB][4],
                                         v4f (&o)[8][kQB]) {
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
+    for (int db = 0; db < kDB; ++db) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const bf16x8 vop = read_vt(vbase, v_rd, db, j);
