@@ -224,7 +224,11 @@ __device__ __forceinline__ void key_loop(Wave<kDB>& w, unsigned char* smem) {
         // slot 1
         if (t + 1 < nt) w.load_k8(lds, t + 1);
         if constexpr (!kB) {
-            if (t < nt) qk_tile<kDC>(smem + kLdsK + cur * kTileBytes, w.k_rd, w.q, s);
+            if (t < nt) {
+                mfma_phase_begin();
+                qk_tile<kDC>(smem + kLdsK + cur * kTileBytes, w.k_rd, w.q, s);
+                mfma_phase_end();
+            }
         } else {
             if (t >= 1) {
                 exp_blocks<kSplit, 8>(w, s, nk_p);
@@ -238,8 +242,10 @@ __device__ __forceinline__ void key_loop(Wave<kDB>& w, unsigned char* smem) {
             if (t < nt) softmax_head<kSplit>(w, s, nk_t);
         } else {
             if (t >= 1) {
+                mfma_phase_begin();
                 pv_tile<kDB>(smem + kLdsV + prev * kTileBytes, w.v_rd, pop, w.o);
                 row_sums(pop, w.l);
+                mfma_phase_end();
             }
         }
         wait_async_loads();
@@ -253,14 +259,20 @@ __device__ __forceinline__ void key_loop(Wave<kDB>& w, unsigned char* smem) {
             }
             if (t + 1 < nt) w.convert_k(smem, prev);
         } else {
-            if (t < nt) qk_tile<kDC>(smem + kLdsK + cur * kTileBytes, w.k_rd, w.q, s);
+            if (t < nt) {
+                mfma_phase_begin();
+                qk_tile<kDC>(smem + kLdsK + cur * kTileBytes, w.k_rd, w.q, s);
+                mfma_phase_end();
+            }
         }
         __syncthreads();
         // slot 4
         if constexpr (!kB) {
             if (t < nt) {
+                mfma_phase_begin();
                 pv_tile<kDB>(smem + kLdsV + cur * kTileBytes, w.v_rd, pop, w.o);
                 row_sums(pop, w.l);
+                mfma_phase_end();
             }
         } else {
             if (t < nt) softmax_head<kSplit>(w, s, nk_t);

@@ -113,7 +113,11 @@ __device__ __forceinline__ void key_loop(Wave& w, unsigned char* smem) {
         // slot 1
         if (t + 1 < nt) w.load_k(lds, t + 1, prev);
         if constexpr (!kB) {
-            if (t < nt) qk_tile(smem + kLdsK + cur * kTileBytes, w.k_rd, w.q, s);
+            if (t < nt) {
+                mfma_phase_begin();
+                qk_tile(smem + kLdsK + cur * kTileBytes, w.k_rd, w.q, s);
+                mfma_phase_end();
+            }
         } else {
             if (t >= 1) pack_tile<kSplit>(w, s, nk_p, pop, w.l);
         }
@@ -122,7 +126,11 @@ __device__ __forceinline__ void key_loop(Wave& w, unsigned char* smem) {
         if constexpr (!kB) {
             if (t < nt) softmax_head<kSplit>(w, s, nk_t);
         } else {
-            if (t >= 1) pv_tile(smem + kLdsV + prev * kTileBytes, w.v_rd, pop, w.o);
+            if (t >= 1) {
+                mfma_phase_begin();
+                pv_tile(smem + kLdsV + prev * kTileBytes, w.v_rd, pop, w.o);
+                mfma_phase_end();
+            }
         }
         wait_async_loads();
         __syncthreads();
@@ -131,12 +139,20 @@ __device__ __forceinline__ void key_loop(Wave& w, unsigned char* smem) {
         if constexpr (!kB) {
             if (t < nt) pack_tile<kSplit>(w, s, nk_t, pop, w.l);
         } else {
-            if (t < nt) qk_tile(smem + kLdsK + cur * kTileBytes, w.k_rd, w.q, s);
+            if (t < nt) {
+                mfma_phase_begin();
+                qk_tile(smem + kLdsK + cur * kTileBytes, w.k_rd, w.q, s);
+                mfma_phase_end();
+            }
         }
         __syncthreads();
         // slot 4
         if constexpr (!kB) {
-            if (t < nt) pv_tile(smem + kLdsV + cur * kTileBytes, w.v_rd, pop, w.o);
+            if (t < nt) {
+                mfma_phase_begin();
+                pv_tile(smem + kLdsV + cur * kTileBytes, w.v_rd, pop, w.o);
+                mfma_phase_end();
+            }
         } else {
             if (t < nt) softmax_head<kSplit>(w, s, nk_t);
         }

@@ -193,6 +193,15 @@ __device__ inline uint32_t v_operand_offset(int r16, int g) {
     return (4 * (uint32_t)g + e) * kRow + 8 * c + 32 * (4 * ((uint32_t)g & 1) + e);
 }
 
+// Waves w and w + 4 share a SIMD, and in every slot one of them runs an MFMA
+// phase (Q K^T or P V) while the other runs exponentials, packing or code
+// conversion.  Without a hint the SIMD favours the older wave,
+// so group B's MFMA phases drew out behind A's vector work; raising the
+// priority of whichever wave is in an MFMA phase keeps the matrix pipe fed and
+// leaves the vector work to fill its gaps.
+__device__ __forceinline__ void mfma_phase_begin() { __builtin_amdgcn_s_setprio(1); }
+__device__ __forceinline__ void mfma_phase_end() { __builtin_amdgcn_s_setprio(0); }
+
 // S = K Q^T for one key tile over the first kDC 32-dim chunks of the head
 // (the rest are zero padding when head_dim < 128): s[kb][qb] holds keys
 // 16kb + 4g + i of query r16.  The K operands of block kb + 1 are requested
