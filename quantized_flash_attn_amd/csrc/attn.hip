@@ -27,8 +27,11 @@
 //     end of the sequence are outside the buffer descriptor's range and
 //     arrive as zeros (their scores are masked).  Once per tile, the wave
 //     group that is busy with VALU work converts the codes exactly to bf16
-//     (every E4M3 value is a bf16 value) into double-buffered bf16 K and V
-//     tiles, the layout of the BF16 baseline kernel (attn_common.h).
+//     (every E4M3 value is a bf16 value) into double-buffered bf16 tiles:
+//     K in the layout of the BF16 baseline kernel (attn_common.h), V
+//     transposed (V^T, read by transposed 8-bit LDS reads of the staged
+//     codes), so that both products read their LDS operands with
+//     ds_read_b128.
 //
 // Ping-pong schedule.  Waves 0-3 (group A) and 4-7 (group B) share the four
 // SIMDs pairwise.  Each key tile takes four barrier-separated slots, and B
@@ -38,7 +41,7 @@
 //   A    S_t = K_t Q^T    p_t (head)      p_t (tail),     O += P_t V_t
 //                                         K_{t+1} -> bf16
 //   B    p_{t-1} (tail),  O += P V_{t-1}  S_t = K_t Q^T   p_t (head)
-//        V_t -> bf16
+//        V_t -> bf16 V^T
 //
 //   S = K Q^T       bf16 MFMA on the exactly converted codes.  gfx950's fp8
 //                   MFMAs add each group of 8 products on a window of about
@@ -51,8 +54,8 @@
 //                   a running row max that only moves when a tile's max
 //                   exceeds it by more than 0.5 log2 units (most tiles skip
 //                   the rescale).
-//   O^T += V^T P^T  bf16 MFMA: A = V^T read with ds_read_b64_tr_b16 from the
-//                   converted V, B = P^T straight from the S accumulator
+//   O^T += V^T P^T  bf16 MFMA: A = V^T read with ds_read_b128 from the
+//                   converted V^T, B = P^T straight from the S accumulator
 //                   layout, rounded to bf16.  Two E4M3 terms of p (hi + lo)
 //                   on the fp8 MFMA would cost the same matrix time plus two
 //                   slow conversions per pair of p; one E4M3 term is too
@@ -71,7 +74,7 @@ namespace {
 
 using namespace attn;
 
-// LDS map (bytes): two bf16 K tiles | two bf16 V tiles | K code staging |
+// LDS map (bytes): two bf16 K tiles | two bf16 V^T tiles | K code staging |
 // V code staging = 160 KiB.
 constexpr int kCodeTile = kBN * kD;   // 16 KiB of E4M3 codes
 constexpr int kLdsK = 0;
@@ -119,25 +122,97 @@ __device__ inline void issue_code_tile_load(const uint8_t* __restrict__ src, uin
     }
 }
 
-// Staged codes -> one bf16 tile, by the 256 threads of one wave group:
+// Staged K codes -> one bf16 K tile, by the 256 threads of one wave group:
 // thread u converts the 16-code chunks ci = u + 256r (r = 0..3), i.e. row
 // ci >> 3, codes 16 (ci & 7) .. + 15, into logical bf16 chunks 2 (ci & 7) and
-// 2 (ci & 7) + 1 of that row, stored at chunk ^ swz(row).  The staging reads
-// are consecutive 16-byte chunks; for K (swz_k) a quarter wave's two rows
-// 2m and 2m + 1 write chunk positions of opposite parity, 16 distinct
-// positions per store.
-template <bool kIsV>
-__device__ __forceinline__ void convert_tile(const unsigned char* src, unsigned char* dst, uint32_t u) {
+// 2 (ci & 7) + 1 of that row, stored at chunk ^ swz_k(row).  The staging
+// reads are consecutive 16-byte chunks; a quarter wave's two rows 2m and
+// 2m + 1 write chunk positions of opposite parity, 16 distinct positions per
+// store.
+__device__ __forceinline__ void convert_k_tile(const unsigned char* src, unsigned char* dst, uint32_t u) {
     u32x4 w[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) w[r] = *(const u32x4*)(src + 16 * (u + 256 * r));
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const uint32_t ci = u + 256 * r, row = ci >> 3, j = ci & 7;
-        const uint32_t swz = kIsV ? swz_v(row) : swz_k(row);
+        const uint32_t swz = swz_k(row);
         unsigned char* d = dst + row * kRow;
         *(bf16x8*)(d + 16 * ((2 * j) ^ swz)) = codes_to_bf16x8(w[r][0], w[r][1]);
         *(bf16x8*)(d + 16 * ((2 * j + 1) ^ swz)) = codes_to_bf16x8(w[r][2], w[r][3]);
+    }
+}
+
+// ---- V^T tiles ----
+// The converted V is stored transposed, as V^T [128 dims][128 keys] bf16 in
+// 256-byte rows, so that P V reads its A operand with ds_read_b128 like
+// Q K^T does (half the LDS instructions of transposed 8-byte reads).  Within
+// each 32-key chunk j the keys are permuted into the order of the P^T
+// operand: logical 16-byte chunk 4j + g of row d holds, at element 4hh + i,
+// key 32j + 16hh + 4g + i of dim d.  Chunk c of row d sits at c ^ swz_vt(d).
+// swz_vt is a bijection on d & 15 (16 distinct positions for the 16 rows one
+// operand read touches) and maps 8 consecutive rows to positions of one
+// parity, so the conversion's stores (8 rows x 2 adjacent chunks) also hit
+// 16 distinct positions.
+__device__ inline uint32_t swz_vt(uint32_t d) { return ((d & 7) << 1) | ((d >> 3) & 1); }
+
+// V code staging is swizzled at 16-byte granularity: logical chunk q of tile
+// row k sits at chunk q ^ swz_v8(k).  The conversion's transposed reads take
+// one 8-byte column slice of 16 rows whose bits 1, 2 and 4 (with bit 0)
+// take every value once; swz_v8 spreads them over 16 distinct 8-byte slots.
+__device__ inline uint32_t swz_v8(uint32_t k) { return ((k >> 1) & 3) | ((k >> 2) & 4); }
+
+// Staged V codes -> one V^T tile, by the 256 threads of one wave group.
+// ds_read_b64_tr_b8: in each 16-lane group, lane r receives byte e (e = 0..7)
+// from the address of lane 2e + (r >> 3), at offset r & 7 (measured).  Read n
+// (0..7) of 16-lane group G of wave gw converts dims 16n + 8 h8 + 0..7 of
+// 32-key chunk j = gw and chunk pair gp (g = 2gp, 2gp + 1), with h8 = G & 1
+// and gp = G >> 1: source lane s points at key row 32j + 8gp + 16(s >> 3) +
+// 4(s & 1) + ((s >> 1) & 3), so that lane r receives, for dim 16n + 8 h8 +
+// (r & 7) and g = 2gp + (r >> 3), keys 32j + 16hh + 4g + i at element
+// 4hh + i: one logical V^T chunk, stored with one ds_write_b128.  The two
+// groups of a half wave read opposite 8-byte halves of the staged chunks,
+// so each read touches every bank once.
+__device__ __forceinline__ void convert_vt(const unsigned char* src, unsigned char* dst, uint32_t u) {
+    typedef int v2i __attribute__((ext_vector_type(2)));
+    const uint32_t gw = u >> 6, G = (u >> 4) & 3, r = u & 15;
+    const uint32_t j = gw, gp = G >> 1, h8 = G & 1;
+    const uint32_t krow = 32 * j + 8 * gp + 16 * (r >> 3) + 4 * (r & 1) + ((r >> 1) & 3);
+    const uint32_t src_off = krow * kD + 16 * swz_v8(krow) + 8 * h8;
+    const uint32_t d_lo = 8 * h8 + (r & 7);
+    const uint32_t dst_off = d_lo * kRow + 16 * ((4 * j + 2 * gp + (r >> 3)) ^ swz_vt(d_lo));
+    v2i x[8];
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+        x[n] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) v2i*)(lds_u8*)(src + (src_off ^ (uint32_t)(n << 4))));
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+        *(bf16x8*)(dst + dst_off + n * 16 * kRow) = codes_to_bf16x8((uint32_t)x[n][0], (uint32_t)x[n][1]);
+}
+
+// O^T += V^T P^T for one key tile over the first kDB 16-dim blocks, V^T read
+// from a converted V^T tile: the A operand of dim block db and key chunk j
+// is row 16db + r16, logical chunk 4j + g, at vt_rd ^ (j << 6) (+ 16 rows per
+// block).  Each operand is requested three steps before its MFMAs issue (the
+// scheduling fence keeps it there), so LDS latency overlaps the matrix work.
+template <int kDB>
+__device__ __forceinline__ void pv_tile_t(const unsigned char* vtbase, uint32_t vt_rd, const bf16x8 (&pop)[kQB][4],
+                                          v4f (&o)[8][kQB]) {
+    constexpr int kSteps = 4 * kDB;   // step n: dim block n >> 2, key chunk n & 3
+    constexpr int kAhead = 3;
+    auto operand = [&](int n) {
+        return *(const bf16x8*)(vtbase + (vt_rd ^ (uint32_t)((n & 3) << 6)) + (n >> 2) * 16 * kRow);
+    };
+    bf16x8 vop[4];
+#pragma unroll
+    for (int n = 0; n < kAhead; ++n) vop[n] = operand(n);
+#pragma unroll
+    for (int n = 0; n < kSteps; ++n) {
+        if (n + kAhead < kSteps) vop[(n + kAhead) & 3] = operand(n + kAhead);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) o[n >> 2][qb] = mfma_bf16(vop[n & 3], pop[qb][n & 3], o[n >> 2][qb]);
     }
 }
 
@@ -178,8 +253,8 @@ struct Wave {
     uint32_t row_stride;   // bytes between tokens of one head (uniform)
     int h, seq_lo, seq_hi, nt, nk_last, wave;
     float cexp;            // s_q s_k log2(e) / sqrt(D)
-    uint32_t k_rd, v_rd;   // operand offsets inside a bf16 K / V tile
-    uint32_t g_ld;         // async loads: row-in-segment * stride + 16-byte chunk
+    uint32_t k_rd, vt_rd;  // operand offsets inside a bf16 K / V^T tile
+    uint32_t g_ld, g_ldv;  // async loads of K / V codes: row-in-segment * stride + 16-byte chunk
     uint32_t cv;           // conversion: thread index inside its group
     int g4;                // 4 g: first key row of this lane inside a 16-key block
     bf16x8 q[kQB][4];      // Q operand (B of S = K Q^T)
@@ -191,13 +266,13 @@ struct Wave {
         issue_code_tile_load(k8, row_stride, h, seq_lo + t * kBN, seq_hi, lds + kLdsK8, wave, g_ld);
     }
     __device__ __forceinline__ void load_v8(lds_u8* lds, int t) const {
-        issue_code_tile_load(v8, row_stride, h, seq_lo + t * kBN, seq_hi, lds + kLdsV8, wave, g_ld);
+        issue_code_tile_load(v8, row_stride, h, seq_lo + t * kBN, seq_hi, lds + kLdsV8, wave, g_ldv);
     }
     __device__ __forceinline__ void convert_k(unsigned char* smem, int buf) const {
-        convert_tile<false>(smem + kLdsK8, smem + kLdsK + buf * kTileBytes, cv);
+        convert_k_tile(smem + kLdsK8, smem + kLdsK + buf * kTileBytes, cv);
     }
     __device__ __forceinline__ void convert_v(unsigned char* smem, int buf) const {
-        convert_tile<true>(smem + kLdsV8, smem + kLdsV + buf * kTileBytes, cv);
+        convert_vt(smem + kLdsV8, smem + kLdsV + buf * kTileBytes, cv);
     }
 };
 
@@ -243,7 +318,7 @@ __device__ __forceinline__ void key_loop(Wave<kDB>& w, unsigned char* smem) {
         } else {
             if (t >= 1) {
                 mfma_phase_begin();
-                pv_tile<kDB>(smem + kLdsV + prev * kTileBytes, w.v_rd, pop, w.o);
+                pv_tile_t<kDB>(smem + kLdsV + prev * kTileBytes, w.vt_rd, pop, w.o);
                 row_sums(pop, w.l);
                 mfma_phase_end();
             }
@@ -270,7 +345,7 @@ __device__ __forceinline__ void key_loop(Wave<kDB>& w, unsigned char* smem) {
         if constexpr (!kB) {
             if (t < nt) {
                 mfma_phase_begin();
-                pv_tile<kDB>(smem + kLdsV + cur * kTileBytes, w.v_rd, pop, w.o);
+                pv_tile_t<kDB>(smem + kLdsV + cur * kTileBytes, w.vt_rd, pop, w.o);
                 row_sums(pop, w.l);
                 mfma_phase_end();
             }
@@ -313,9 +388,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     w.wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in an SGPR
     const bool group_b = w.wave >= kWaves / 2;          // wave-uniform
     w.k_rd = k_operand_offset(r16, g);
-    w.v_rd = v_operand_offset(r16, g);
-    // Async loads: lane covers row lane >> 3 of each 8-row segment, chunk lane & 7.
+    w.vt_rd = (uint32_t)(r16 * kRow + 16 * ((uint32_t)g ^ swz_vt((uint32_t)r16)));
+    // Async loads: lane covers row lane >> 3 of each 8-row segment, LDS chunk
+    // lane & 7.  K is staged unswizzled; for V the lane fetches the logical
+    // chunk (lane & 7) ^ swz_v8(row), where the tile row 16 wave + 8r +
+    // (lane >> 3) has bit 4 = wave & 1 for both of the wave's segments.
     w.g_ld = ((uint32_t)lane >> 3) * w.row_stride + ((uint32_t)lane & 7) * 16;
+    w.g_ldv = ((uint32_t)lane >> 3) * w.row_stride +
+              16 * (((uint32_t)lane & 7) ^ swz_v8(((uint32_t)lane >> 3) + 16 * ((uint32_t)w.wave & 1)));
     w.cv = (uint32_t)tid & (kGroupThreads - 1);
     w.g4 = 4 * g;
 
