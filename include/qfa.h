@@ -88,6 +88,7 @@ typedef struct qfa_scale_snapshot {
     float inv[3];                   /* fp32(448 / max(amax_eff, 2^-100)) */
     int32_t cursor;                 /* dynamic forwards so far */
     int32_t history_len;
+    int32_t requantized[3];         /* 1 if the last dynamic forward quantized tensor t a second time */
 } qfa_scale_snapshot;
 
 /* Bytes of device memory a scale state needs (a few KiB). */
@@ -124,6 +125,12 @@ qfa_status qfa_init_scale_state(qfa_scale_state* st, void* device_buf, int histo
  *     saturated to +-448, sign of zero kept.
  *   q, k, v      device bf16 [total_tokens, num_heads, head_dim]
  *   q8, k8, v8   device uint8 E4M3 codes, same shape (out)
+ * Dynamic mode reads each tensor once when amax_t does not exceed the ring
+ * maximum over the slots other than the one being replaced: it quantizes with
+ * that maximum's scale while taking amax_t, and the result is then exactly the
+ * one defined above.  Otherwise (the first forwards, or a new maximum over the
+ * window) it quantizes tensor t a second time with the new scale;
+ * qfa_scale_snapshot.requantized[t] says which happened.
  * total_tokens may be 0 (the forward still records amax 0 in dynamic mode).
  * Forwards on one state must be ordered on one stream (single-writer ring);
  * distinct states are independent.

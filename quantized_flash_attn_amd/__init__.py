@@ -84,6 +84,7 @@ class _Snapshot(ctypes.Structure):
         ("inv", ctypes.c_float * 3),
         ("cursor", ctypes.c_int32),
         ("history_len", ctypes.c_int32),
+        ("requantized", ctypes.c_int32 * 3),
     ]
 
 
@@ -312,7 +313,7 @@ def bf16_varlen_attn(q, k, v, cu_seqlens, num_heads=None, head_dim=HEAD_DIM, out
 
 
 def read_scale_state(state: ScaleState) -> dict:
-    """Synchronous copy of the device state (ring, cursor, amax, descale, inv)."""
+    """Synchronous copy of the device state (ring, cursor, amax, descale, inv, requantized)."""
     snap = _Snapshot()
     with torch.cuda.device(state.buffer.device):
         _check(_lib.qfa_read_scale_state(state.handle, ctypes.byref(snap), _stream_ptr(state.buffer.device)))
@@ -325,6 +326,7 @@ def read_scale_state(state: ScaleState) -> dict:
         "inv": [float(x) for x in snap.inv],
         "cursor": int(snap.cursor),
         "history_len": hist,
+        "requantized": [int(x) for x in snap.requantized],
     }
 
 

@@ -234,6 +234,7 @@ qfa_status qfa_read_scale_state(const qfa_scale_state* st, qfa_scale_snapshot* o
     memcpy(out->inv, h.inv, sizeof(out->inv));
     out->cursor = h.cursor;
     out->history_len = h.history_len;
+    memcpy(out->requantized, h.requantized, sizeof(out->requantized));
     return ok();
 }
 

@@ -23,8 +23,9 @@ struct DeviceState {
     float inv[3];                     // quantization factors
     float static_eff[3];              // fp32(static_amax * margin)
     int32_t cursor;                   // dynamic forwards so far
-    int32_t cursor_snap;              // cursor as the current forward's amax pass found it
     int32_t history_len;              // 1..16
+    int32_t requantized[3];           // 1 if the last dynamic forward needed the second pass for tensor t
+    int32_t cursor_snap;              // cursor as the current forward's first pass found it
     alignas(16) uint32_t partial[3][kMaxPartials];  // per-workgroup max of |bf16| bit patterns
 };
 static_assert(offsetof(DeviceState, partial) % 16 == 0, "partials must be 16-byte aligned");

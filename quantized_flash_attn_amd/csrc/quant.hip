@@ -8,21 +8,27 @@
 // times a margin.  Quantization ("FP8 ViT Encoder Attention", intro) turns
 // Q/K/V into FP8 before the attention call.
 //
-// Kernels (both HBM-streaming):
-//   amax_partial_kernel    grid (P, 3): max of |x| as bf16 bit patterns,
-//                          one partial per workgroup, no atomics; workgroup
-//                          (0, 0) also snapshots the ring cursor.  Its loads
-//                          allocate in the caches (unlike quantize's
-//                          streaming loads), so that quantize, which reads
-//                          the same tensors right after, finds part of them
-//                          in the 256 MB Infinity Cache.
-//   quantize_kernel        grid (G, 3): x * inv -> clamp +-448 -> E4M3 (RNE).
-//                          Dynamic mode: every workgroup first reduces its
-//                          tensor's partials and derives the forward's scale
-//                          from the ring itself (all workgroups compute the
-//                          same value); workgroup (0, t) is the only writer of
-//                          ring slot, cursor and scales.  No atomics.
-//   amax_packed_kernel,    the same two steps reading Q, K and V straight out
+// Dynamic mode makes one pass over the data in the usual case.  The
+// forward's effective amax is max(amax_t, the ring slots other than the one
+// being replaced), and the second operand is known before the pass.  So:
+//   amax_quantize_kernel   grid (P, 3): streams tensor t once, quantizing
+//                          with the scale of that speculative amax (the
+//                          other slots' maximum) while taking max|x| as bf16
+//                          bit patterns; one partial per workgroup, no
+//                          atomics; workgroup (0, 0) snapshots the cursor.
+//   requantize_kernel      grid (R, 3): every workgroup reduces the partials
+//                          and derives the forward's scale from the ring
+//                          (all agree); workgroup (0, t) is the only writer
+//                          of ring slot, cursor and scales.  If amax_t did
+//                          not exceed the speculative amax, the scale is the
+//                          one already used and the codes stand (bit for bit
+//                          the codes of a separate amax pass); otherwise the
+//                          tensor is quantized again with the new scale.
+//                          The second pass runs on the first forwards and
+//                          when a tensor sets a new maximum over the window.
+//   quantize_kernel<true>  grid (G, 3): static mode, x * inv -> clamp +-448
+//                          -> E4M3 (RNE) with the loaded scales.
+//   amax_packed_kernel,    amax, then quantize, reading Q, K and V straight out
 //   quantize_packed_kernel of a fused QKV projection output [T, 3, H, D]
 //                          (D <= 128) and writing codes [T, H, 128] whose dims
 //                          past D are zero, the layout the attention kernel
@@ -65,6 +71,7 @@ __global__ void init_state_kernel(DeviceState* st, int history_len, float e0, fl
         st->descale[t] = d;
         st->inv[t] = i;
         st->static_eff[t] = t == 0 ? e0 : (t == 1 ? e1 : e2);
+        st->requantized[t] = 0;
     }
     if (t == 0) {
         st->cursor = 0;
@@ -90,53 +97,33 @@ __device__ inline uint32_t max_abs_bits(u32x4 w, uint32_t m) {
     return m;
 }
 
-__global__ __launch_bounds__(kThreads) void amax_partial_kernel(const u32x4* __restrict__ q, const u32x4* __restrict__ k,
-                                                                const u32x4* __restrict__ v, int64_t n_chunks,
-                                                                DeviceState* st) {
-    const int t = blockIdx.y;
-    uint32_t* __restrict__ partial = &st->partial[0][0];
-    // The ring cursor as this forward finds it; the quantize kernel reads the
-    // snapshot while its workgroup (0, 0) advances the cursor itself.
-    if (blockIdx.x == 0 && t == 0 && threadIdx.x == 0) st->cursor_snap = st->cursor;
-    const u32x4* __restrict__ src = t == 0 ? q : (t == 1 ? k : v);
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    uint32_t m = 0;
-    for (; i + 3 * stride < n_chunks; i += 4 * stride) {
-        const u32x4 a = src[i];
-        const u32x4 b = src[i + stride];
-        const u32x4 c = src[i + 2 * stride];
-        const u32x4 d = src[i + 3 * stride];
-        m = max_abs_bits(a, m);
-        m = max_abs_bits(b, m);
-        m = max_abs_bits(c, m);
-        m = max_abs_bits(d, m);
-    }
-    for (; i < n_chunks; i += stride) m = max_abs_bits(src[i], m);
-    m = wave_max_u32(m);
-    __shared__ uint32_t red[kThreads / 64];
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t r = red[0];
-#pragma unroll
-        for (int w = 1; w < kThreads / 64; ++w) r = max(r, red[w]);
-        partial[t * kMaxPartials + blockIdx.x] = r;
-    }
+// Ring maximum over the slots other than the one this forward replaces
+// (slot cursor % history_len): the effective amax of the forward is the
+// maximum of this and amax_t.  Uniform over the workgroup.
+__device__ inline float ring_max_others(const DeviceState* st, int t, int cursor) {
+    const int hist = st->history_len;
+    const int slot = cursor % hist;
+    float m = 0.0f;
+    for (int j = 0; j < hist; ++j)
+        if (j != slot) m = fmaxf(m, st->ring[t][j]);
+    return m;
 }
 
-// The forward's scale for tensor t, derived inside every quantize workgroup
-// from state written before this kernel started (the amax partials, the
-// ring and the cursor snapshot), so all workgroups agree without
+// The forward's scale for tensor t, derived inside every workgroup of the
+// second kernel from state written before it started (the amax partials,
+// the ring and the cursor snapshot), so all workgroups agree without
 // synchronising.  amax_t = max of the partials; the ring's slot
 // cursor % history_len receives amax_t, so the effective amax is the maximum
 // of amax_t and the other slots (the slot being replaced is excluded: its
-// old value leaves the window).  Workgroup (0, t) writes the slot, the
-// scales and (t = 0) the incremented cursor; nobody else reads those fields
-// during this kernel, and its readers exclude the slot, so there is no race.
-__device__ float dynamic_inv(DeviceState* st, int t, int n_partials) {
+// old value leaves the window).  *again is set when amax_t exceeds the other
+// slots' maximum, i.e. when the scale differs from the one the first pass
+// used.  Workgroup (0, t) writes the slot, the scales, the requantized flag
+// and (t = 0) the incremented cursor; nobody else reads those fields during
+// this kernel, and its readers exclude the slot, so there is no race.
+__device__ float dynamic_inv(DeviceState* st, int t, int n_partials, bool* again) {
     __shared__ uint32_t red[kThreads / 64];
     __shared__ float sh_inv;
+    __shared__ int sh_again;
     const int lane = threadIdx.x & 63;
     // This thread's partials (indices past the last are clamped to it: a
     // repeated value does not change the maximum), all loaded before use.
@@ -160,24 +147,28 @@ __device__ float dynamic_inv(DeviceState* st, int t, int n_partials) {
 #pragma unroll
         for (int w = 1; w < kThreads / 64; ++w) bits = max(bits, red[w]);
         const float amax = __uint_as_float(bits << 16);
-        float eff = fmaxf(amax, rv);
+        float others = rv;
 #pragma unroll
-        for (int off = 8; off >= 1; off >>= 1) eff = fmaxf(eff, __shfl_xor(eff, off));  // max over lanes 0..15
+        for (int off = 8; off >= 1; off >>= 1) others = fmaxf(others, __shfl_xor(others, off));  // lanes 0..15
+        const float eff = fmaxf(amax, others);
         if (lane == 0) {
             float d, i;
             scales_from_amax(eff, &d, &i);
             sh_inv = i;
+            sh_again = amax > others;
             if (blockIdx.x == 0) {
                 st->ring[t][slot] = amax;
                 st->amax_observed[t] = amax;
                 st->amax_eff[t] = eff;
                 st->descale[t] = d;
                 st->inv[t] = i;
+                st->requantized[t] = amax > others;
                 if (t == 0) st->cursor = cursor + 1;
             }
         }
     }
     __syncthreads();
+    *again = sh_again != 0;
     return sh_inv;
 }
 
@@ -204,72 +195,65 @@ __device__ inline u32x2 quantize8(u32x4 w, float inv) {
     return out;
 }
 
-template <bool kStatic>
-__global__ __launch_bounds__(kThreads) void quantize_kernel(DeviceState* st, const u32x4* __restrict__ q,
-                                                            const u32x4* __restrict__ k, const u32x4* __restrict__ v,
-                                                            int64_t n_chunks, u32x2* __restrict__ q8,
-                                                            u32x2* __restrict__ k8, u32x2* __restrict__ v8,
-                                                            int n_partials) {
-    const int t = blockIdx.y;
-    float inv;
-    if constexpr (kStatic) {
-        const float eff = st->static_eff[t];
-        float d;
-        scales_from_amax(eff, &d, &inv);
-        // The static factors do not depend on the data: workgroup 0 records
-        // them; every workgroup derives the same value from static_eff.
-        if (blockIdx.x == 0 && threadIdx.x == 0) {
-            st->amax_eff[t] = eff;
-            st->descale[t] = d;
-            st->inv[t] = inv;
-        }
-    } else {
-        inv = dynamic_inv(st, t, n_partials);
+// Where tensor t's chunks come from and go to.  A chunk is 8 bf16 in and 8
+// codes out; n() chunks per tensor.
+//   Split: three [T, H, D] tensors, chunk i of tensor t at src_t + i.
+//   Packed: a fused [T, 3, H, D] projection output (D <= 128) into codes
+//   [T, H, 128]: output chunk o is dims 8 (o & 15) .. + 7 of head row o >> 4
+//   = token * H + h; the first cph = D / 8 chunks of a row come from input
+//   chunk (token * 3 + t) * cpr + h * cph + (o & 15), cpr = H * cph, the rest
+//   are zero.
+struct SplitIO {
+    const u32x4* src;
+    u32x2* dst;
+    int64_t count;
+    __device__ int64_t n() const { return count; }
+    __device__ u32x4 load(int64_t i) const { return __builtin_nontemporal_load(src + i); }
+    __device__ void store(int64_t i, u32x2 c) const { __builtin_nontemporal_store(c, dst + i); }
+};
+
+struct PackedIO {
+    const u32x4* qkv;
+    u32x2* dst;
+    uint32_t out_chunks, num_heads, cph, cpr, t;
+    __device__ int64_t n() const { return out_chunks; }
+    __device__ u32x4 load(int64_t i) const {
+        const uint32_t o = (uint32_t)i, row = o >> 4, dc = o & 15;
+        if (dc >= cph) return u32x4{0u, 0u, 0u, 0u};
+        const uint32_t token = row / num_heads, h = row - token * num_heads;
+        return __builtin_nontemporal_load(qkv + ((size_t)token * 3 + t) * cpr + h * cph + dc);
     }
-    const u32x4* __restrict__ src = t == 0 ? q : (t == 1 ? k : v);
-    u32x2* __restrict__ dst = t == 0 ? q8 : (t == 1 ? k8 : v8);
+    __device__ void store(int64_t i, u32x2 c) const { __builtin_nontemporal_store(c, dst + i); }
+};
+
+// Grid-stride pass over this workgroup's chunks with four chunks in flight
+// per thread: codes with factor inv and, if kMax, the running max|x| bits.
+template <bool kMax, class IO>
+__device__ inline uint32_t stream_pass(const IO& io, float inv) {
+    const int64_t n = io.n();
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    for (; i + 3 * stride < n_chunks; i += 4 * stride) {
-        const u32x4 a = __builtin_nontemporal_load(src + i);
-        const u32x4 b = __builtin_nontemporal_load(src + i + stride);
-        const u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
-        const u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
-        __builtin_nontemporal_store(quantize8(a, inv), dst + i);
-        __builtin_nontemporal_store(quantize8(b, inv), dst + i + stride);
-        __builtin_nontemporal_store(quantize8(c, inv), dst + i + 2 * stride);
-        __builtin_nontemporal_store(quantize8(d, inv), dst + i + 3 * stride);
+    uint32_t m = 0;
+    for (; i + 3 * stride < n; i += 4 * stride) {
+        u32x4 x[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] = io.load(i + r * stride);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if constexpr (kMax) m = max_abs_bits(x[r], m);
+            io.store(i + r * stride, quantize8(x[r], inv));
+        }
     }
-    for (; i < n_chunks; i += stride) __builtin_nontemporal_store(quantize8(__builtin_nontemporal_load(src + i), inv), dst + i);
+    for (; i < n; i += stride) {
+        const u32x4 x = io.load(i);
+        if constexpr (kMax) m = max_abs_bits(x, m);
+        io.store(i, quantize8(x, inv));
+    }
+    return m;
 }
 
-// Packed input: tensor t's chunk i (8 consecutive bf16 of one head row) is
-// chunk (token * 3 + t) * cpr + w of the [T, 3, H, D] array, with
-// token = i / cpr, w = i % cpr and cpr = H * D / 8 chunks per (token, tensor).
-__global__ __launch_bounds__(kThreads) void amax_packed_kernel(const u32x4* __restrict__ qkv, uint32_t n_chunks,
-                                                               uint32_t cpr, DeviceState* st) {
-    const int t = blockIdx.y;
-    uint32_t* __restrict__ partial = &st->partial[0][0];
-    if (blockIdx.x == 0 && t == 0 && threadIdx.x == 0) st->cursor_snap = st->cursor;
-    const uint32_t stride = gridDim.x * kThreads;
-    auto src = [&](uint32_t i) {
-        const uint32_t token = i / cpr, w = i - token * cpr;
-        return qkv + ((size_t)token * 3 + t) * cpr + w;
-    };
-    uint32_t m = 0;
-    uint32_t i = blockIdx.x * kThreads + threadIdx.x;
-    // four independent loads in flight per thread (i + 3 stride < n_chunks < 2^31: no overflow)
-    for (; i + 3 * stride < n_chunks; i += 4 * stride) {
-        const u32x4 a = *src(i);
-        const u32x4 b = *src(i + stride);
-        const u32x4 c = *src(i + 2 * stride);
-        const u32x4 d = *src(i + 3 * stride);
-        m = max_abs_bits(a, m);
-        m = max_abs_bits(b, m);
-        m = max_abs_bits(c, m);
-        m = max_abs_bits(d, m);
-    }
-    for (; i < n_chunks; i += stride) m = max_abs_bits(*src(i), m);
+// Workgroup maximum of m -> partial[t][blockIdx.x].
+__device__ inline void store_partial(DeviceState* st, int t, uint32_t m) {
     m = wave_max_u32(m);
     __shared__ uint32_t red[kThreads / 64];
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
@@ -278,59 +262,108 @@ __global__ __launch_bounds__(kThreads) void amax_packed_kernel(const u32x4* __re
         uint32_t r = red[0];
 #pragma unroll
         for (int w = 1; w < kThreads / 64; ++w) r = max(r, red[w]);
-        partial[t * kMaxPartials + blockIdx.x] = r;
+        st->partial[t][blockIdx.x] = r;
     }
 }
 
-// Output chunk o of tensor t (8 codes) is dims 8 (o & 15) .. + 7 of head row
-// o >> 4 = token * H + h of the [T, H, 128] codes; the first cph = D / 8
-// chunks of a row come from the packed input, the rest are zero.
-template <bool kStatic>
-__global__ __launch_bounds__(kThreads) void quantize_packed_kernel(DeviceState* st, const u32x4* __restrict__ qkv,
-                                                                   uint32_t n_out_chunks, uint32_t num_heads,
-                                                                   uint32_t cph, u32x2* __restrict__ q8,
-                                                                   u32x2* __restrict__ k8, u32x2* __restrict__ v8,
-                                                                   int n_partials) {
+// First pass: codes with the scale of the other slots' maximum, and the
+// amax partial.  Workgroup (0, 0) snapshots the ring cursor, which the
+// second kernel reads while its workgroup (0, 0) advances the cursor.
+template <class IO>
+__device__ inline void amax_quantize(DeviceState* st, const IO& io) {
     const int t = blockIdx.y;
-    float inv;
-    if constexpr (kStatic) {
-        const float eff = st->static_eff[t];
-        float d;
-        scales_from_amax(eff, &d, &inv);
-        if (blockIdx.x == 0 && threadIdx.x == 0) {
-            st->amax_eff[t] = eff;
-            st->descale[t] = d;
-            st->inv[t] = inv;
-        }
-    } else {
-        inv = dynamic_inv(st, t, n_partials);
+    const int cursor = st->cursor;
+    float d, inv;
+    scales_from_amax(ring_max_others(st, t, cursor), &d, &inv);
+    const uint32_t m = stream_pass<true>(io, inv);
+    if (blockIdx.x == 0 && t == 0 && threadIdx.x == 0) st->cursor_snap = cursor;
+    store_partial(st, t, m);
+}
+
+// Second pass: the forward's scale; quantize tensor t again only if it
+// differs from the first pass's.
+template <class IO>
+__device__ inline void requantize(DeviceState* st, const IO& io, int n_partials) {
+    bool again;
+    const float inv = dynamic_inv(st, blockIdx.y, n_partials, &again);
+    if (again) stream_pass<false>(io, inv);
+}
+
+// The static factors do not depend on the data: workgroup 0 records them;
+// every workgroup derives the same value from static_eff.
+__device__ inline float static_inv(DeviceState* st, int t) {
+    const float eff = st->static_eff[t];
+    float d, inv;
+    scales_from_amax(eff, &d, &inv);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        st->amax_eff[t] = eff;
+        st->descale[t] = d;
+        st->inv[t] = inv;
     }
-    u32x2* __restrict__ dst = t == 0 ? q8 : (t == 1 ? k8 : v8);
-    const uint32_t cpr = num_heads * cph;
-    const uint32_t stride = gridDim.x * kThreads;
-    // Input chunk of output chunk o (valid when (o & 15) < cph).
-    auto src = [&](uint32_t o) {
-        const uint32_t row = o >> 4, dc = o & 15;
-        const uint32_t token = row / num_heads, h = row - token * num_heads;
-        return qkv + ((size_t)token * 3 + t) * cpr + h * cph + dc;
-    };
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    uint32_t o = blockIdx.x * kThreads + threadIdx.x;
-    // four independent chunks in flight per thread (o + 3 stride < n_out_chunks < 2^31: no overflow)
-    for (; o + 3 * stride < n_out_chunks; o += 4 * stride) {
-        u32x4 x[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const uint32_t oo = o + r * stride;
-            x[r] = (oo & 15) < cph ? __builtin_nontemporal_load(src(oo)) : zero;
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) __builtin_nontemporal_store(quantize8(x[r], inv), dst + o + r * stride);
-    }
-    for (; o < n_out_chunks; o += stride) {
-        const u32x4 x = (o & 15) < cph ? __builtin_nontemporal_load(src(o)) : zero;
-        __builtin_nontemporal_store(quantize8(x, inv), dst + o);
-    }
+    return inv;
+}
+
+__device__ inline SplitIO split_io(const u32x4* q, const u32x4* k, const u32x4* v, u32x2* q8, u32x2* k8, u32x2* v8,
+                                   int64_t n_chunks) {
+    const int t = blockIdx.y;
+    return SplitIO{t == 0 ? q : (t == 1 ? k : v), t == 0 ? q8 : (t == 1 ? k8 : v8), n_chunks};
+}
+
+__device__ inline PackedIO packed_io(const u32x4* qkv, u32x2* q8, u32x2* k8, u32x2* v8, uint32_t out_chunks,
+                                     uint32_t num_heads, uint32_t cph) {
+    const uint32_t t = blockIdx.y;
+    return PackedIO{qkv, t == 0 ? q8 : (t == 1 ? k8 : v8), out_chunks, num_heads, cph, num_heads * cph, t};
+}
+
+__global__ __launch_bounds__(kThreads) void amax_quantize_kernel(DeviceState* st, const u32x4* __restrict__ q,
+                                                                 const u32x4* __restrict__ k,
+                                                                 const u32x4* __restrict__ v, int64_t n_chunks,
+                                                                 u32x2* __restrict__ q8, u32x2* __restrict__ k8,
+                                                                 u32x2* __restrict__ v8) {
+    amax_quantize(st, split_io(q, k, v, q8, k8, v8, n_chunks));
+}
+
+__global__ __launch_bounds__(kThreads) void requantize_kernel(DeviceState* st, const u32x4* __restrict__ q,
+                                                              const u32x4* __restrict__ k, const u32x4* __restrict__ v,
+                                                              int64_t n_chunks, u32x2* __restrict__ q8,
+                                                              u32x2* __restrict__ k8, u32x2* __restrict__ v8,
+                                                              int n_partials) {
+    requantize(st, split_io(q, k, v, q8, k8, v8, n_chunks), n_partials);
+}
+
+__global__ __launch_bounds__(kThreads) void quantize_static_kernel(DeviceState* st, const u32x4* __restrict__ q,
+                                                                   const u32x4* __restrict__ k,
+                                                                   const u32x4* __restrict__ v, int64_t n_chunks,
+                                                                   u32x2* __restrict__ q8, u32x2* __restrict__ k8,
+                                                                   u32x2* __restrict__ v8) {
+    const float inv = static_inv(st, blockIdx.y);
+    stream_pass<false>(split_io(q, k, v, q8, k8, v8, n_chunks), inv);
+}
+
+__global__ __launch_bounds__(kThreads) void amax_quantize_packed_kernel(DeviceState* st, const u32x4* __restrict__ qkv,
+                                                                        uint32_t out_chunks, uint32_t num_heads,
+                                                                        uint32_t cph, u32x2* __restrict__ q8,
+                                                                        u32x2* __restrict__ k8,
+                                                                        u32x2* __restrict__ v8) {
+    amax_quantize(st, packed_io(qkv, q8, k8, v8, out_chunks, num_heads, cph));
+}
+
+__global__ __launch_bounds__(kThreads) void requantize_packed_kernel(DeviceState* st, const u32x4* __restrict__ qkv,
+                                                                     uint32_t out_chunks, uint32_t num_heads,
+                                                                     uint32_t cph, u32x2* __restrict__ q8,
+                                                                     u32x2* __restrict__ k8, u32x2* __restrict__ v8,
+                                                                     int n_partials) {
+    requantize(st, packed_io(qkv, q8, k8, v8, out_chunks, num_heads, cph), n_partials);
+}
+
+__global__ __launch_bounds__(kThreads) void quantize_static_packed_kernel(DeviceState* st,
+                                                                          const u32x4* __restrict__ qkv,
+                                                                          uint32_t out_chunks, uint32_t num_heads,
+                                                                          uint32_t cph, u32x2* __restrict__ q8,
+                                                                          u32x2* __restrict__ k8,
+                                                                          u32x2* __restrict__ v8) {
+    const float inv = static_inv(st, blockIdx.y);
+    stream_pass<false>(packed_io(qkv, q8, k8, v8, out_chunks, num_heads, cph), inv);
 }
 
 int grid_for(int64_t n_chunks, int64_t chunks_per_thread, int cap) {
@@ -351,15 +384,17 @@ hipError_t launch_init_state(DeviceState* st, int history_len, const float stati
 hipError_t launch_quantize_dynamic(DeviceState* st, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                    int64_t n, uint8_t* q8, uint8_t* k8, uint8_t* v8, hipStream_t s) {
     const int64_t chunks = n / 8;
-    // Grid shapes from a sweep at 1 x 8192 tokens, 16 heads (amax: 256
-    // workgroups per tensor, each thread streaming >= 8 chunks; quantize: 16
-    // chunks per thread): 74 % of HBM peak for the pair, against 66 % with
-    // 4x more, thinner workgroups (whose scale prologue then dominates).
-    const int ga = grid_for(chunks, 8, kMaxPartials);
-    amax_partial_kernel<<<dim3(ga, 3), kThreads, 0, s>>>((const u32x4*)q, (const u32x4*)k, (const u32x4*)v, chunks, st);
-    const int gq = grid_for(chunks, 16, 2048);
-    quantize_kernel<false><<<dim3(gq, 3), kThreads, 0, s>>>(st, (const u32x4*)q, (const u32x4*)k, (const u32x4*)v,
-                                                           chunks, (u32x2*)q8, (u32x2*)k8, (u32x2*)v8, ga);
+    // One partial per first-pass workgroup (at most kMaxPartials per tensor,
+    // each thread streaming >= 8 chunks).  The second pass uses the same grid:
+    // a smaller one costs the same when it only derives the scale (about 2.5 us
+    // at 1 x 8192 tokens, 16 heads) and streams slower when it quantizes again
+    // (53 us with 256 workgroups per tensor, 60 with 64, 83 with 32).
+    const int g = grid_for(chunks, 8, kMaxPartials);
+    amax_quantize_kernel<<<dim3(g, 3), kThreads, 0, s>>>(st, (const u32x4*)q, (const u32x4*)k, (const u32x4*)v, chunks,
+                                                         (u32x2*)q8, (u32x2*)k8, (u32x2*)v8);
+    requantize_kernel<<<dim3(g, 3), kThreads, 0, s>>>(st, (const u32x4*)q, (const u32x4*)k,
+                                                                         (const u32x4*)v, chunks, (u32x2*)q8,
+                                                                         (u32x2*)k8, (u32x2*)v8, g);
     return hipGetLastError();
 }
 
@@ -369,32 +404,29 @@ hipError_t launch_quantize_dynamic(DeviceState* st, const uint16_t* q, const uin
 hipError_t launch_quantize_packed(DeviceState* st, bool dynamic, const uint16_t* qkv, int64_t total_tokens,
                                   int num_heads, int head_dim, uint8_t* q8, uint8_t* k8, uint8_t* v8, hipStream_t s) {
     const uint32_t cph = (uint32_t)head_dim / 8;
-    const uint32_t cpr = (uint32_t)num_heads * cph;
-    const uint32_t in_chunks = (uint32_t)total_tokens * cpr;            // per tensor
     const uint32_t out_chunks = (uint32_t)total_tokens * (uint32_t)num_heads * 16;
-    int ga = 1;
     if (dynamic) {
-        ga = grid_for(in_chunks, 8, kMaxPartials);
-        amax_packed_kernel<<<dim3(ga, 3), kThreads, 0, s>>>((const u32x4*)qkv, in_chunks, cpr, st);
-    }
-    const int gq = grid_for(out_chunks, 16, 2048);
-    if (dynamic)
-        quantize_packed_kernel<false><<<dim3(gq, 3), kThreads, 0, s>>>(st, (const u32x4*)qkv, out_chunks,
-                                                                       (uint32_t)num_heads, cph, (u32x2*)q8,
-                                                                       (u32x2*)k8, (u32x2*)v8, ga);
-    else
-        quantize_packed_kernel<true><<<dim3(gq, 3), kThreads, 0, s>>>(st, (const u32x4*)qkv, out_chunks,
+        const int g = grid_for(out_chunks, 8, kMaxPartials);
+        amax_quantize_packed_kernel<<<dim3(g, 3), kThreads, 0, s>>>(st, (const u32x4*)qkv, out_chunks,
+                                                                    (uint32_t)num_heads, cph, (u32x2*)q8, (u32x2*)k8,
+                                                                    (u32x2*)v8);
+        requantize_packed_kernel<<<dim3(g, 3), kThreads, 0, s>>>(
+            st, (const u32x4*)qkv, out_chunks, (uint32_t)num_heads, cph, (u32x2*)q8, (u32x2*)k8, (u32x2*)v8, g);
+    } else {
+        const int g = grid_for(out_chunks, 16, 2048);
+        quantize_static_packed_kernel<<<dim3(g, 3), kThreads, 0, s>>>(st, (const u32x4*)qkv, out_chunks,
                                                                       (uint32_t)num_heads, cph, (u32x2*)q8,
-                                                                      (u32x2*)k8, (u32x2*)v8, 1);
+                                                                      (u32x2*)k8, (u32x2*)v8);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_quantize_static(DeviceState* st, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                   int64_t n, uint8_t* q8, uint8_t* k8, uint8_t* v8, hipStream_t s) {
     const int64_t chunks = n / 8;
-    const int gq = grid_for(chunks, 16, 2048);
-    quantize_kernel<true><<<dim3(gq, 3), kThreads, 0, s>>>(st, (const u32x4*)q, (const u32x4*)k, (const u32x4*)v,
-                                                          chunks, (u32x2*)q8, (u32x2*)k8, (u32x2*)v8, 1);
+    const int g = grid_for(chunks, 16, 2048);
+    quantize_static_kernel<<<dim3(g, 3), kThreads, 0, s>>>(st, (const u32x4*)q, (const u32x4*)k, (const u32x4*)v,
+                                                           chunks, (u32x2*)q8, (u32x2*)k8, (u32x2*)v8);
     return hipGetLastError();
 }
 

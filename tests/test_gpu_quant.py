@@ -150,3 +150,73 @@ def test_workload_quantize(widx):
             _check_forward_codes(w, fwd, xs, outs, inv, full)
             del xs, outs
         log(f"  ok: final amax_eff {snap['amax_eff']}")
+
+
+def _with_amax(shape, amax, seed):
+    """bf16 tensor of ``shape`` with values in (-amax/4, amax/4) and one element equal to -amax (so max|x| = amax)."""
+    g = torch.Generator().manual_seed(seed)
+    x = (torch.rand(shape, generator=g) - 0.5) * (amax / 2)
+    x.view(-1)[int(torch.randint(0, x.numel(), (1,), generator=g))] = -amax
+    return x.to(torch.bfloat16)
+
+
+# Per-forward amax of Q, K and V with a ring of 4 slots.  Q walks through: the
+# first forward (empty ring), amax below the other slots' maximum, a new
+# maximum, that maximum leaving the window (the scale drops with no second
+# pass), an amax equal to the other slots' maximum, and a new maximum once more.
+_AMAX_SEQ = {
+    0: [2.0, 1.0, 1.5, 3.0, 1.0, 2.5, 0.5, 1.0, 2.5, 2.625],
+    1: [0.25, 0.5, 1.0, 2.0, 4.0, 8.0, 16.0, 32.0, 64.0, 128.0],
+    2: [5.0, 5.0, 5.0, 5.0, 5.0, 5.0, 5.0, 5.0, 5.0, 5.0],
+}
+
+
+def _expected_requant(ost, observed):
+    """From the oracle's ring before this forward: a second pass is needed when amax_t exceeds the maximum of the
+    slots other than the one this forward replaces (only then does the scale differ from the one known in advance)."""
+    keep = np.arange(ost.history_len) != ost.cursor % ost.history_len
+    others = ost.ring[:, keep].max(axis=1) if keep.any() else np.zeros(3, np.float32)
+    return [int(np.float32(observed[t]) > others[t]) for t in range(3)]
+
+
+@pytest.mark.parametrize("T,H", [(300, 2), (4096, 16)])
+def test_single_pass_and_second_pass(T, H):
+    """Codes, ring and scales bit-exact on every forward, whichever pass produced them, and the
+    requantized flag as the ring dictates."""
+    st = qfa.init_scale_state(DEV, history_len=4)
+    ost = oracle.ScaleState(history_len=4)
+    seen = set()
+    for fwd in range(len(_AMAX_SEQ[0])):
+        xs = [_with_amax((T, H, 128), _AMAX_SEQ[t][fwd], seed=31 * fwd + t) for t in range(3)]
+        observed = [oracle.amax(bf16_to_f32(x)) for x in xs]
+        want_requant = _expected_requant(ost, observed)
+        outs = qfa.quantize_qkv(st, "dynamic", *[x.to(DEV) for x in xs])
+        _, inv = ost.forward_dynamic(observed)
+        snap = qfa.read_scale_state(st)
+        _state_equal(snap, ost)
+        assert snap["requantized"] == want_requant, (fwd, snap["requantized"], want_requant)
+        seen.update(want_requant)
+        for t in range(3):
+            got = codes(outs[t])
+            want = oracle.quantize(bf16_to_f32(xs[t]), inv[t])
+            assert np.array_equal(got, want), (fwd, t, int(np.count_nonzero(got != want)))
+    assert seen == {0, 1}
+
+
+def test_single_pass_packed():
+    """The same sequence through the fused [T, 3, H, D] entry point (D = 80)."""
+    T, H, D = 777, 3, 80
+    st = qfa.init_scale_state(DEV, history_len=4)
+    ost = oracle.ScaleState(history_len=4)
+    for fwd in range(len(_AMAX_SEQ[0])):
+        xs = [_with_amax((T, H, D), _AMAX_SEQ[t][fwd], seed=77 * fwd + t) for t in range(3)]
+        qkv = torch.stack(xs, dim=1).contiguous()
+        observed = [oracle.amax(bf16_to_f32(x)) for x in xs]
+        want_requant = _expected_requant(ost, observed)
+        g = qfa.quantize_qkv_packed(st, "dynamic", qkv.to(DEV))
+        o8q, o8k, o8v, descale, _ = oracle.quantize_qkv_packed(ost, "dynamic", bf16_to_f32(qkv))
+        snap = qfa.read_scale_state(st)
+        assert snap["requantized"] == want_requant, (fwd, snap["requantized"], want_requant)
+        assert np.array_equal(np.array(snap["descale"], np.float32), descale)
+        for gg, oo in zip(g, (o8q, o8k, o8v)):
+            assert np.array_equal(codes(gg), oo), fwd
