@@ -102,9 +102,10 @@ __device__ inline bf16x8 codes_to_bf16x8(uint32_t w0, uint32_t w1) {
 }
 
 // Asynchronous fetch of one 128-key tile of codes into a staging buffer
-// ([key][128] rows of 128 B, unswizzled): wave w fills the 1 KiB segments 2w
-// and 2w + 1 (tile rows [16w, 16w + 16)); lane l of a segment writes LDS
-// bytes [16l, 16l + 16), i.e. row l >> 3 of the segment, chunk l & 7.  Each
+// ([key][128] rows of 128 B, 16-byte chunks permuted within each row by the
+// lane offsets): wave w fills the 1 KiB segments 2w and 2w + 1 (tile rows
+// [16w, 16w + 16)); lane l of a segment writes LDS bytes [16l, 16l + 16),
+// i.e. row l >> 3 of the segment, chunk l & 7.  Each
 // segment's buffer descriptor starts at this head's slice of its first row
 // and ends after the last row of the sequence: rows past it are out of
 // range, which the hardware turns into zeros in LDS.
@@ -122,24 +123,28 @@ __device__ inline void issue_code_tile_load(const uint8_t* __restrict__ src, uin
     }
 }
 
-// Staged K codes -> one bf16 K tile, by the 256 threads of one wave group:
-// thread u converts the 16-code chunks ci = u + 256r (r = 0..3), i.e. row
-// ci >> 3, codes 16 (ci & 7) .. + 15, into logical bf16 chunks 2 (ci & 7) and
-// 2 (ci & 7) + 1 of that row, stored at chunk ^ swz_k(row).  The staging
-// reads are consecutive 16-byte chunks; a quarter wave's two rows 2m and
-// 2m + 1 write chunk positions of opposite parity, 16 distinct positions per
-// store.
+// Staged K codes -> one bf16 K tile, by the 256 threads of one wave group.
+// Each 16-lane group converts the rows 2m and 2m + 1 (m = (u >> 4) + 16r,
+// r = 0..3): lanes 0..3 take 16-code chunks j = 0..3 of row 2m, lanes 4..7
+// the same chunks of row 2m + 1, lanes 8..15 chunks 4..7 of both, and each
+// chunk becomes logical bf16 chunks 2j and 2j + 1 of its row, stored at
+// chunk ^ swz_k(row).  The K staging holds chunk q of row k at q ^ 4 (k & 1)
+// (async-load lane offsets), so every group of 8 lanes reads 8 distinct
+// 16-byte slots of a 128-byte window and stores to 8 distinct chunks modulo
+// 8 (the LDS bank layout is described at swz_vt).
 __device__ __forceinline__ void convert_k_tile(const unsigned char* src, unsigned char* dst, uint32_t u) {
+    const uint32_t q = u & 15, j = (q & 3) + 4 * (q >> 3);
+    const uint32_t row0 = 2 * (u >> 4) + ((q >> 2) & 1);   // row of r = 0; r adds 32 rows
+    const uint32_t rd = row0 * kD + 16 * (j ^ (4 * (row0 & 1)));
+    const uint32_t swz = swz_k(row0);                       // the same for row0 + 32r
+    unsigned char* d = dst + row0 * kRow;
     u32x4 w[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) w[r] = *(const u32x4*)(src + 16 * (u + 256 * r));
+    for (int r = 0; r < 4; ++r) w[r] = *(const u32x4*)(src + rd + r * 32 * kD);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const uint32_t ci = u + 256 * r, row = ci >> 3, j = ci & 7;
-        const uint32_t swz = swz_k(row);
-        unsigned char* d = dst + row * kRow;
-        *(bf16x8*)(d + 16 * ((2 * j) ^ swz)) = codes_to_bf16x8(w[r][0], w[r][1]);
-        *(bf16x8*)(d + 16 * ((2 * j + 1) ^ swz)) = codes_to_bf16x8(w[r][2], w[r][3]);
+        *(bf16x8*)(d + r * 32 * kRow + 16 * ((2 * j) ^ swz)) = codes_to_bf16x8(w[r][0], w[r][1]);
+        *(bf16x8*)(d + r * 32 * kRow + 16 * ((2 * j + 1) ^ swz)) = codes_to_bf16x8(w[r][2], w[r][3]);
     }
 }
 
@@ -150,37 +155,38 @@ __device__ __forceinline__ void convert_k_tile(const unsigned char* src, unsigne
 // each 32-key chunk j the keys are permuted into the order of the P^T
 // operand: logical 16-byte chunk 4j + g of row d holds, at element 4hh + i,
 // key 32j + 16hh + 4g + i of dim d.  Chunk c of row d sits at c ^ swz_vt(d).
-// swz_vt is a bijection on d & 15 (16 distinct positions for the 16 rows one
-// operand read touches) and maps 8 consecutive rows to positions of one
-// parity, so the conversion's stores (8 rows x 2 adjacent chunks) also hit
-// 16 distinct positions.
-__device__ inline uint32_t swz_vt(uint32_t d) { return ((d & 7) << 1) | ((d >> 3) & 1); }
+//
+// LDS banks, as the bank-conflict counter measures them: 32 banks of 4
+// bytes over a 128-byte window; a 16-byte-per-lane access is served 8
+// lanes at a time and an 8-byte one 16 lanes at a time.  An access is
+// conflict-free when each such lane group touches distinct 16-byte (8-byte)
+// slots modulo 128 bytes.  Rows are 256 bytes, so only the chunk index
+// modulo 8 picks the banks: swz_vt(d) = d & 15 (the K layout) gives the 8
+// rows of an operand read, and of a conversion store, 8 distinct chunks.
+__device__ inline uint32_t swz_vt(uint32_t d) { return d & 15; }
 
 // V code staging is swizzled at 16-byte granularity: logical chunk q of tile
-// row k sits at chunk q ^ swz_v8(k).  The conversion's transposed reads take
-// one 8-byte column slice of 16 rows whose bits 1, 2 and 4 (with bit 0)
-// take every value once; swz_v8 spreads them over 16 distinct 8-byte slots.
-__device__ inline uint32_t swz_v8(uint32_t k) { return ((k >> 1) & 3) | ((k >> 2) & 4); }
+// row k sits at chunk q ^ swz_v8(k).  A transposed read takes one 16-byte
+// column chunk of the 8 rows {32j + 16hh + 4g + i}; swz_v8 maps their bits
+// 0, 1 and 4 to distinct chunks, and row bit 2 (g's low bit) flips chunk bit
+// 0 so that neighbouring lane groups use the other chunks as well.
+__device__ inline uint32_t swz_v8(uint32_t k) { return ((k & 3) | ((k >> 2) & 4)) ^ ((k >> 2) & 1); }
 
 // Staged V codes -> one V^T tile, by the 256 threads of one wave group.
 // ds_read_b64_tr_b8: in each 16-lane group, lane r receives byte e (e = 0..7)
 // from the address of lane 2e + (r >> 3), at offset r & 7 (measured).  Read n
-// (0..7) of 16-lane group G of wave gw converts dims 16n + 8 h8 + 0..7 of
-// 32-key chunk j = gw and chunk pair gp (g = 2gp, 2gp + 1), with h8 = G & 1
-// and gp = G >> 1: source lane s points at key row 32j + 8gp + 16(s >> 3) +
-// 4(s & 1) + ((s >> 1) & 3), so that lane r receives, for dim 16n + 8 h8 +
-// (r & 7) and g = 2gp + (r >> 3), keys 32j + 16hh + 4g + i at element
-// 4hh + i: one logical V^T chunk, stored with one ds_write_b128.  The two
-// groups of a half wave read opposite 8-byte halves of the staged chunks,
-// so each read touches every bank once.
+// (0..7) of 16-lane group G of wave gw converts dims 16n .. 16n + 15 of
+// 32-key chunk j = gw for g = G: source lane s points at key row
+// 32j + 16(s >> 3) + 4g + ((s >> 1) & 3), at the low (s even) or high (s odd)
+// 8 bytes of the row's 16-byte chunk n, so that lane r receives, for dim
+// 16n + r, keys 32j + 16hh + 4g + i at element 4hh + i: logical V^T chunk
+// 4j + g of row 16n + r, stored with one ds_write_b128.
 __device__ __forceinline__ void convert_vt(const unsigned char* src, unsigned char* dst, uint32_t u) {
     typedef int v2i __attribute__((ext_vector_type(2)));
-    const uint32_t gw = u >> 6, G = (u >> 4) & 3, r = u & 15;
-    const uint32_t j = gw, gp = G >> 1, h8 = G & 1;
-    const uint32_t krow = 32 * j + 8 * gp + 16 * (r >> 3) + 4 * (r & 1) + ((r >> 1) & 3);
-    const uint32_t src_off = krow * kD + 16 * swz_v8(krow) + 8 * h8;
-    const uint32_t d_lo = 8 * h8 + (r & 7);
-    const uint32_t dst_off = d_lo * kRow + 16 * ((4 * j + 2 * gp + (r >> 3)) ^ swz_vt(d_lo));
+    const uint32_t j = u >> 6, g = (u >> 4) & 3, r = u & 15;
+    const uint32_t krow = 32 * j + 16 * (r >> 3) + 4 * g + ((r >> 1) & 3);
+    const uint32_t src_off = krow * kD + 16 * swz_v8(krow) + 8 * (r & 1);
+    const uint32_t dst_off = r * kRow + 16 * ((4 * j + g) ^ swz_vt(r));
     v2i x[8];
 #pragma unroll
     for (int n = 0; n < 8; ++n)
@@ -390,10 +396,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     w.k_rd = k_operand_offset(r16, g);
     w.vt_rd = (uint32_t)(r16 * kRow + 16 * ((uint32_t)g ^ swz_vt((uint32_t)r16)));
     // Async loads: lane covers row lane >> 3 of each 8-row segment, LDS chunk
-    // lane & 7.  K is staged unswizzled; for V the lane fetches the logical
-    // chunk (lane & 7) ^ swz_v8(row), where the tile row 16 wave + 8r +
-    // (lane >> 3) has bit 4 = wave & 1 for both of the wave's segments.
-    w.g_ld = ((uint32_t)lane >> 3) * w.row_stride + ((uint32_t)lane & 7) * 16;
+    // lane & 7, and fetches the logical chunk that the staging swizzle puts
+    // there: (lane & 7) ^ 4 (row & 1) for K; (lane & 7) ^ swz_v8(row) for V,
+    // where the tile row 16 wave + 8r + (lane >> 3) has bit 4 = wave & 1 for
+    // both of the wave's segments.
+    w.g_ld = ((uint32_t)lane >> 3) * w.row_stride + 16 * (((uint32_t)lane & 7) ^ (4 * (((uint32_t)lane >> 3) & 1)));
     w.g_ldv = ((uint32_t)lane >> 3) * w.row_stride +
               16 * (((uint32_t)lane & 7) ^ swz_v8(((uint32_t)lane >> 3) + 16 * ((uint32_t)w.wave & 1)));
     w.cv = (uint32_t)tid & (kGroupThreads - 1);
