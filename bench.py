@@ -422,6 +422,23 @@ def main():
     # the BF16 baseline on the same inputs (the pages state FP8 gains as BF16 -> FP8 pairs)
     ms_bf16 = timed(lambda i: qfa.bf16_varlen_attn(*sets[i % len(sets)], cu, H, out=out), args.steps, 0.1)
 
+    def per_launch(fn, n):
+        """p10 / p50 / p90 of single launches (events around each launch on the launch stream), in ms."""
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(ev):
+            a.record(stream)
+            fn(i)
+            b.record(stream)
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) for a, b in ev)
+        pick = lambda q: t[min(n - 1, int(round(q * (n - 1))))]
+        return {"p10": round(pick(0.1), 4), "p50": round(pick(0.5), 4), "p90": round(pick(0.9), 4), "launches": n}
+
+    n_dist = max(10, min(50, args.steps))
+    dist_attn = per_launch(lambda i: qfa.fp8_varlen_attn(q8, k8, v8, scales, cu, H, out=out), n_dist)
+    dist_quant = per_launch(lambda i: qfa.quantize_qkv(st, "dynamic", *sets[i % len(sets)], q8, k8, v8), n_dist)
+
     flop = w.attn_flop
     value = flop / (ms_step * 1e-3) / 1e12
     attn_tflops = flop / (ms_attn * 1e-3) / 1e12
@@ -449,14 +466,16 @@ def main():
                    "scaling_mode": "dynamic", "history_len": 16, "input_sets": len(sets)},
         "frac_fp8_peak_incl_quant": round(value / FP8_PEAK_TFLOPS, 4),
         "attention": {"ms": round(ms_attn, 4), "tflops": round(attn_tflops, 1),
-                      "frac_fp8_peak": round(attn_tflops / FP8_PEAK_TFLOPS, 4)},
+                      "frac_fp8_peak": round(attn_tflops / FP8_PEAK_TFLOPS, 4),
+                      "exp2_per_s": round(w.exp2_count / (ms_attn * 1e-3), -9),
+                      "per_launch_ms": dist_attn},
         "bf16_attention": {"ms": round(ms_bf16, 4), "tflops": round(flop / (ms_bf16 * 1e-3) / 1e12, 1),
                            "frac_bf16_peak": round(flop / (ms_bf16 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                            "fp8_speedup_incl_quant": round(ms_bf16 / ms_step, 3),
                            "fp8_speedup_attention_only": round(ms_bf16 / ms_attn, 3)},
         "quantize_dynamic": {"ms": round(ms_quant, 4), "algorithmic_bytes": quant_bytes, "gbs": round(quant_gbs, 1),
                              "frac_hbm_peak": round(quant_gbs / HBM_PEAK_GBS, 4),
-                             "second_pass_last_forward": second_pass},
+                             "second_pass_last_forward": second_pass, "per_launch_ms": dist_quant},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / FP8_PEAK_TFLOPS, 4), "traffic": measured_traffic(args.workload),
                      "kernel": "attn_fwd_kernel", "flop_per_launch": flop},

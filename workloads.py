@@ -58,6 +58,11 @@ class Workload:
         """Algorithmic attention work: two matmuls, 2 flop per multiply-add."""
         return int(sum(4 * n * n * self.num_heads * HEAD_DIM for n in self.seqlens))
 
+    @property
+    def exp2_count(self) -> int:
+        """Softmax exponentials of the attention: one per (query, key) pair of a sequence, per head."""
+        return int(sum(n * n * self.num_heads for n in self.seqlens))
+
 
 WORKLOADS = {
     1: Workload(1, "tiny single image, 1x256 tokens, 2 heads", (256,), 2, "unit", "unit", 0.005, 30.0,
