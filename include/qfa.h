@@ -174,7 +174,8 @@ const float* qfa_descale_ptr(const qfa_scale_state* st);
  *                  cu[num_seqs] = total_tokens; empty sequences are allowed
  *   head_dim       8..128 in steps of 8 (128 for qfa_quantize_qkv's codes)
  *   out            device bf16 [total_tokens, num_heads, head_dim] (out)
- * total_tokens must be below 2^31.  The kernel converts the codes exactly to
+ * total_tokens must be below 2^31 and num_heads at most 65536
+ * (QFA_ERR_SHAPE otherwise).  The kernel converts the codes exactly to
  * bf16 and runs both products on bf16 MFMAs with float32 accumulation; the
  * probabilities are rounded to bf16 for the P*V product.
  */
@@ -192,7 +193,8 @@ qfa_status qfa_fp8_varlen_attn(const uint8_t* q8, const uint8_t* k8, const uint8
  *   q, k, v        device bf16 [total_tokens, num_heads, 128]
  *   cu_seqlens     device int32[num_seqs + 1], same rules as qfa_fp8_varlen_attn
  *   out            device bf16 [total_tokens, num_heads, 128] (out)
- * total_tokens must be below 2^31.  Products and sums run in fp32 on bf16
+ * total_tokens must be below 2^31 and num_heads at most 65536.  Products
+ * and sums run in fp32 on bf16
  * MFMA operands; the probabilities are rounded to bf16 for the P*V product.
  * Same status codes as qfa_fp8_varlen_attn.
  */

@@ -172,6 +172,11 @@ const float* qfa_descale_ptr(const qfa_scale_state* st) {
     return ((const qfa::DeviceState*)st->device)->descale;
 }
 
+// The attention kernels fetch up to 128 token rows of one head through a
+// buffer descriptor whose 32-bit range spans those rows at a stride of
+// num_heads * 256 bytes (bf16); 65536 heads keep it below 2^31.
+constexpr int kMaxAttnHeads = 65536;
+
 qfa_status qfa_fp8_varlen_attn(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* scales,
                                const int32_t* cu_seqlens, int num_seqs, int64_t total_tokens, int num_heads,
                                int head_dim, void* out, void* stream) {
@@ -183,6 +188,8 @@ qfa_status qfa_fp8_varlen_attn(const uint8_t* q8, const uint8_t* k8, const uint8
     if (s != QFA_OK) return s;
     if (num_seqs < 1) return fail(QFA_ERR_SHAPE, "%s: num_seqs %d must be at least 1", where, num_seqs);
     if (total_tokens >= (INT64_C(1) << 31)) return fail(QFA_ERR_SHAPE, "%s: total_tokens must be below 2^31", where);
+    if (num_heads > kMaxAttnHeads)
+        return fail(QFA_ERR_SHAPE, "%s: num_heads %d above %d", where, num_heads, kMaxAttnHeads);
     if (!scales || !cu_seqlens) return fail(QFA_ERR_NULL, "%s: null scales or cu_seqlens", where);
     if (n > 0 && (!q8 || !k8 || !v8 || !out)) return fail(QFA_ERR_NULL, "%s: null tensor pointer", where);
     if (n > 0 && !(aligned16(q8) && aligned16(k8) && aligned16(v8) && aligned16(out)))
@@ -205,6 +212,8 @@ qfa_status qfa_bf16_varlen_attn(const void* q, const void* k, const void* v, con
     if (s != QFA_OK) return s;
     if (num_seqs < 1) return fail(QFA_ERR_SHAPE, "%s: num_seqs %d must be at least 1", where, num_seqs);
     if (total_tokens >= (INT64_C(1) << 31)) return fail(QFA_ERR_SHAPE, "%s: total_tokens must be below 2^31", where);
+    if (num_heads > kMaxAttnHeads)
+        return fail(QFA_ERR_SHAPE, "%s: num_heads %d above %d", where, num_heads, kMaxAttnHeads);
     if (!cu_seqlens) return fail(QFA_ERR_NULL, "%s: null cu_seqlens", where);
     if (n > 0 && (!q || !k || !v || !out)) return fail(QFA_ERR_NULL, "%s: null tensor pointer", where);
     if (n > 0 && !(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out)))

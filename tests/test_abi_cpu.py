@@ -112,6 +112,7 @@ def test_attention_validation():
     assert _attn(T=-5) == SHAPE
     assert _attn(B=0) == SHAPE
     assert _attn(T=1 << 31, H=1) == SHAPE
+    assert _attn(T=1, H=65537) == SHAPE     # the tile loads' 32-bit descriptor range bounds the head count
     assert _attn(sc=None) == NULL
     assert _attn(cu=None) == NULL
     for name in ("q8", "k8", "v8", "out"):
@@ -156,6 +157,7 @@ def test_bf16_attention_validation():
     assert _battn(T=-5) == SHAPE
     assert _battn(B=0) == SHAPE
     assert _battn(T=1 << 31, H=1) == SHAPE
+    assert _battn(T=1, H=65537) == SHAPE
     assert _battn(cu=None) == NULL
     for name in ("q", "k", "v", "out"):
         assert _battn(**{name: None}) == NULL
