@@ -25,8 +25,8 @@
 //   * K and V tiles of codes are fetched with buffer_load_dwordx4 ... lds (L2
 //     to LDS without registers) into one staging buffer each; rows past the
 //     end of the sequence are outside the buffer descriptor's range and
-//     arrive as zeros (their scores are masked).  Once per tile, the wave
-//     group that is busy with VALU work converts the codes exactly to bf16
+//     arrive as zeros (their scores are masked).  Once per tile, a wave group
+//     converts the codes exactly to bf16 right after one of its P V products
 //     (every E4M3 value is a bf16 value) into double-buffered bf16 tiles:
 //     K in the layout of the BF16 baseline kernel (attn_common.h), V
 //     transposed (V^T, read by transposed 8-bit LDS reads of the staged

@@ -157,20 +157,15 @@ __device__ __forceinline__ void softmax_head(W& w, v4f (&s)[8][kQB], int nk) {
     exp_blocks<0, kSplit>(w, s, nk);
 }
 
-// The whole step in one piece.
-template <class W>
-__device__ __forceinline__ void exp_phase(W& w, v4f (&s)[8][kQB], int nk) {
-    softmax_head<8>(w, s, nk);
-}
-
-
 // ---- bf16 operand tiles in LDS (both kernels run QK^T and P V on bf16) ----
 //
-// A K or V tile is [128 keys][128 dims] bf16: rows of 256 B, 16 chunks of
-// 16 B; logical chunk c of row r sits at chunk c ^ swz(r).
+// A K tile (both kernels) or V tile (BF16 kernel) is [128 keys][128 dims]
+// bf16: rows of 256 B, 16 chunks of 16 B; logical chunk c of row r sits at
+// chunk c ^ swz(r).
 //   K (A operand of S = K Q^T, ds_read_b128): 16 lanes read rows r..r+15 of
 //     one logical chunk; swz_k(r) = r & 15 spreads them over all 16 chunk
-//     positions (all 64 banks).
+//     positions (all 64 banks), and any 8 consecutive lanes over 8 chunks
+//     distinct modulo 8.
 //   V (V^T operand, ds_read_b64_tr_b16): 32 lanes read 8-byte pieces of
 //     rows {4g + e : g in 0..1, e in 0..3} (+ a multiple of 16), a 32-byte
 //     span per row; swz_v(r) = (r & 7) << 1 moves the span of row r to
