@@ -334,21 +334,32 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_seq8192_h16.json")
 ATTN_SRCS = ("attn.hip", "attn_common.h")     # the attention kernel's sources
 
 
+def code_sha256(path):
+    """SHA-256 of a C++ source with comments and white space removed: it changes when the code does, not when a
+    comment does."""
+    import hashlib
+    import re
+
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return hashlib.sha256(re.sub(r"\s+", "", text).encode()).hexdigest()
+
+
 def measured_traffic(workload_index):
     """HBM bytes per attention launch from the committed rocprofv3 counter summary, or None.
 
-    Only valid for the workload the counters were taken on and while the kernel source is
-    unchanged since (its sha256 is recorded next to the counts)."""
-    import hashlib
-
+    Only valid for the workload the counters were taken on and while the kernel code is
+    unchanged since (code_sha256 of its sources is recorded next to the counts)."""
     if workload_index != 3 or not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as f:
         rec = json.load(f)
+    recorded = rec.get("sources_code_sha256", {})
     for name in ATTN_SRCS:
-        with open(os.path.join(ROOT, "quantized_flash_attn_amd", "csrc", name), "rb") as f:
-            if hashlib.sha256(f.read()).hexdigest() != rec["sources_sha256"].get(name):
-                return None
+        if code_sha256(os.path.join(ROOT, "quantized_flash_attn_amd", "csrc", name)) != recorded.get(name):
+            return None
     return rec["kernels"]["attn_fwd_kernel"]["traffic_bytes"]
 
 
