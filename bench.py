@@ -378,7 +378,7 @@ def main():
         packed_path(args.packed_head_dim, args.steps, args.warmup)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the path runs on one GPU (sharding across GPUs is a design only); --gpus must be 1"}))
         sys.exit(2)
     import numpy as np
     import torch
