@@ -176,3 +176,22 @@ def test_workload_attention(widx):
     ref, mag = oracle.attention_rows(oq8, ok8, ov8, ost.descale, cu, rows, magnitude=True)
     got = bf16_to_f32(out[rows_t])
     assert_attn_close(got, ref, f"workload {widx}", mag=mag)
+
+
+@pytest.mark.parametrize("seqlens", [[0], [0, 0, 0]])
+def test_empty_batch(seqlens):
+    """No tokens at all: both attention entries return an empty output and leave the stream usable."""
+    H = 2
+    cu = cu_seqlens_tensor(seqlens, DEV)
+    st = qfa.init_scale_state(DEV)
+    e = torch.zeros((0, H, 128), dtype=torch.bfloat16, device=DEV)
+    q8, k8, v8 = qfa.quantize_qkv(st, "dynamic", e, e, e)
+    out = qfa.fp8_varlen_attn(q8, k8, v8, qfa.descale(st), cu, H)
+    assert tuple(out.shape) == (0, H, 128)
+    out_b = qfa.bf16_varlen_attn(e, e, e, cu, H)
+    assert tuple(out_b.shape) == (0, H, 128)
+    # a non-empty call right after still works
+    q, k, v = random_qkv([5], H, seed=3, device=DEV)
+    gcodes, got, _ = gpu_path(q, k, v, [5])
+    ocodes, (ref, mag), _ = oracle_path(q, k, v, [5])
+    assert_attn_close(bf16_to_f32(got), ref, "after empty", mag=mag)
