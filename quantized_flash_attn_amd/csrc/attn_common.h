@@ -199,29 +199,29 @@ __device__ __forceinline__ void mfma_phase_end() { __builtin_amdgcn_s_setprio(0)
 
 // S = K Q^T for one key tile over the first kDC 32-dim chunks of the head
 // (the rest are zero padding when head_dim < 128): s[kb][qb] holds keys
-// 16kb + 4g + i of query r16.  The K operands of block kb + 1 are requested
-// before the MFMAs of block kb issue (the scheduling fence keeps them
-// there), so LDS latency overlaps the matrix work.
+// 16kb + 4g + i of query r16.  Step n multiplies K operand n (key block
+// n / kDC, chunk n % kDC) into both query blocks; each operand is requested
+// six steps before its MFMAs issue (the scheduling fence keeps it there), so
+// a wave keeps six 1 KiB LDS reads in flight behind its matrix work.
 template <int kDC = 4>
 __device__ __forceinline__ void qk_tile(const unsigned char* kbase, uint32_t k_rd, const bf16x8 (&q)[kQB][4],
                                         v4f (&s)[8][kQB]) {
-    bf16x8 kop[2][4];
+    constexpr int kSteps = 8 * kDC;
+    constexpr int kAhead = 6;
+    auto operand = [&](int n) {
+        return *(const bf16x8*)(kbase + (k_rd ^ (uint32_t)((n % kDC) << 6)) + (n / kDC) * 16 * kRow);
+    };
+    bf16x8 kop[8];
 #pragma unroll
-    for (int c = 0; c < kDC; ++c) kop[0][c] = *(const bf16x8*)(kbase + (k_rd ^ (uint32_t)(c << 6)));
+    for (int n = 0; n < kAhead; ++n) kop[n] = operand(n);
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb) {
-        if (kb + 1 < 8) {
-#pragma unroll
-            for (int c = 0; c < kDC; ++c)
-                kop[(kb + 1) & 1][c] = *(const bf16x8*)(kbase + (k_rd ^ (uint32_t)(c << 6)) + (kb + 1) * 16 * kRow);
-        }
+    for (int n = 0; n < kSteps; ++n) {
+        if (n + kAhead < kSteps) kop[(n + kAhead) & 7] = operand(n + kAhead);
         __builtin_amdgcn_sched_barrier(0);
+        const int kb = n / kDC, c = n % kDC;
 #pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) s[kb][qb] = v4f{0, 0, 0, 0};
-#pragma unroll
-        for (int c = 0; c < kDC; ++c)
-#pragma unroll
-            for (int qb = 0; qb < kQB; ++qb) s[kb][qb] = mfma_bf16(kop[kb & 1][c], q[qb][c], s[kb][qb]);
+        for (int qb = 0; qb < kQB; ++qb)
+            s[kb][qb] = mfma_bf16(kop[n & 7], q[qb][c], c == 0 ? v4f{0, 0, 0, 0} : s[kb][qb]);
     }
 }
 
