@@ -13,7 +13,7 @@ import torch
 import oracle
 import quantized_flash_attn_amd as qfa
 from helpers import assert_attn_close, bf16_to_f32, codes, log, sample_rows
-from workloads import WORKLOADS, cu_seqlens_tensor, make_qkv, random_qkv
+from workloads import WORKLOADS, cu_seqlens_tensor, make_qkv, ramp_qkv, random_qkv
 
 pytestmark = pytest.mark.gpu
 
@@ -46,6 +46,7 @@ def oracle_path(q, k, v, seqlens, ost=None, mode="dynamic"):
     ([0, 513, 0, 17], 2, 1.5, 0.0),
     ([1000, 24, 389], 3, 2.5, 0.002),
     ([2, 3, 5, 7, 11, 13, 17, 19, 23, 29, 31, 37, 41, 43, 47, 53], 1, 1.0, 0.0),
+    ([256, 257, 384], 2, 1.0, 0.001),
 ])
 def test_small_ragged(seqlens, H, sigma, outliers):
     log(f"seqlens={seqlens} H={H} sigma={sigma}")
@@ -56,6 +57,21 @@ def test_small_ragged(seqlens, H, sigma, outliers):
     for g, o in zip(gcodes, ocodes):
         assert np.array_equal(codes(g), o)
     assert_attn_close(bf16_to_f32(out), ref, f"seqlens {seqlens}", mag=mag)
+
+
+@pytest.mark.parametrize("order", ["increasing", "decreasing"])
+def test_running_max_moves(order):
+    """Logits rising along the keys move the running row max, and rescale O
+    and l, at every key tile, the ragged last tile included; falling logits
+    never move it after the first tile."""
+    seqlens = [1000, 333, 129]
+    log(f"{order} logits, seqlens={seqlens}")
+    q, k, v = ramp_qkv(seqlens, 2, seed=29, device=DEV, order=order)
+    gcodes, out, _ = gpu_path(q, k, v, seqlens)
+    ocodes, (ref, mag), _ = oracle_path(q, k, v, seqlens)
+    for g, o in zip(gcodes, ocodes):
+        assert np.array_equal(codes(g), o)
+    assert_attn_close(bf16_to_f32(out), ref, f"{order} logits", mag=mag)
 
 
 def test_distinct_tensor_scales():

@@ -13,7 +13,7 @@ import torch
 import oracle
 import quantized_flash_attn_amd as qfa
 from helpers import TOL_MAX_BF16, TOL_MEAN_BF16, assert_attn_close, bf16_to_f32, log, sample_rows
-from workloads import WORKLOADS, cu_seqlens_tensor, make_qkv, random_qkv
+from workloads import WORKLOADS, cu_seqlens_tensor, make_qkv, ramp_qkv, random_qkv
 
 pytestmark = pytest.mark.gpu
 
@@ -33,6 +33,7 @@ def _close(got, ref, what, mag):
     ([0, 513, 0, 17], 2, 1.5, 0.0),
     ([1000, 24, 389], 3, 2.5, 0.002),
     ([2, 3, 5, 7, 11, 13, 17, 19, 23, 29, 31, 37, 41, 43, 47, 53], 1, 1.0, 0.0),
+    ([256, 257, 384], 2, 1.0, 0.001),
 ])
 def test_small_ragged(seqlens, H, sigma, outliers):
     log(f"bf16 seqlens={seqlens} H={H} sigma={sigma}")
@@ -42,6 +43,18 @@ def test_small_ragged(seqlens, H, sigma, outliers):
     cu = np.concatenate([[0], np.cumsum(seqlens)])
     ref, mag = oracle.attention_float(*(bf16_to_f32(t) for t in (q, k, v)), cu, magnitude=True)
     _close(bf16_to_f32(out), ref, f"seqlens {seqlens}", mag)
+
+
+@pytest.mark.parametrize("order", ["increasing", "decreasing"])
+def test_running_max_moves(order):
+    """Logits rising along the keys rescale O and l at every key tile; falling ones never after the first."""
+    seqlens = [1000, 333, 129]
+    log(f"bf16 {order} logits, seqlens={seqlens}")
+    q, k, v = ramp_qkv(seqlens, 2, seed=31, device=DEV, order=order)
+    out = qfa.bf16_varlen_attn(q, k, v, cu_seqlens_tensor(seqlens, DEV), 2)
+    cu = np.concatenate([[0], np.cumsum(seqlens)])
+    ref, mag = oracle.attention_float(*(bf16_to_f32(t) for t in (q, k, v)), cu, magnitude=True)
+    _close(bf16_to_f32(out), ref, f"{order} logits", mag)
 
 
 def test_one_token_sequence_returns_v_row():

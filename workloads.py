@@ -130,3 +130,30 @@ def random_qkv(seqlens, num_heads, seed, device="cpu", sigma=1.0, outlier_p=0.0,
     shape = (T, num_heads, HEAD_DIM)
     sig = torch.full((num_heads,), float(sigma), dtype=torch.float32)
     return tuple(_draw(shape, sig, outlier_p, outlier_scale, seed + t, device) for t in range(3))
+
+
+def ramp_qkv(seqlens, num_heads, seed, device="cpu", order="increasing") -> tuple:
+    """Seeded bf16 Q, K, V whose logits move steadily along each sequence.
+
+    Every query of a head is a small perturbation of one positive direction
+    u_h (entries in [1, 2)), and key j of a sequence of n tokens is
+    u_h * s_j with s_j rising from 0.05 to 1 over the sequence (``order``
+    "increasing") or falling from 1 to 0.05 ("decreasing").  The scaled
+    logits then grow by about 4.5 log2 units per 128 keys of a 1000-token
+    sequence (faster in shorter ones) for the increasing order, so the
+    running row max moves at every key tile, and never after the first tile
+    for the decreasing one.  V is N(0, 1).
+    """
+    T = int(sum(seqlens))
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    u = 1.0 + torch.rand((num_heads, HEAD_DIM), generator=g)
+    q = u.expand(T, num_heads, HEAD_DIM) * (1.0 + 0.05 * torch.randn((T, num_heads, HEAD_DIM), generator=g))
+    s = []
+    for n in seqlens:
+        r = torch.linspace(0.05, 1.0, int(n)) if int(n) > 1 else torch.ones(int(n))
+        s.append(r if order == "increasing" else r.flip(0))
+    s = torch.cat(s) if s else torch.zeros(0)
+    k = u.expand(T, num_heads, HEAD_DIM) * s.view(-1, 1, 1)
+    v = torch.randn((T, num_heads, HEAD_DIM), generator=g)
+    return tuple(t.to(torch.bfloat16).to(device) for t in (q, k, v))
