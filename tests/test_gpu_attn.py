@@ -74,6 +74,23 @@ def test_running_max_moves(order):
     assert_attn_close(bf16_to_f32(out), ref, f"{order} logits", mag=mag)
 
 
+def test_many_short_sequences():
+    """About 1500 sequences of 0..40 tokens with a few longer ones: many
+    sequences per query tile range, empty sequences, and one spare virtual
+    tile per sequence in the tile -> sequence search."""
+    g = np.random.default_rng(37)
+    seqlens = [int(n) for n in g.integers(0, 41, size=1500)]
+    for pos, n in ((100, 257), (700, 513), (1400, 300)):
+        seqlens[pos] = n
+    log(f"{len(seqlens)} sequences, {sum(seqlens)} tokens")
+    q, k, v = random_qkv(seqlens, 2, seed=41, device=DEV, sigma=1.5, outlier_p=0.001, outlier_scale=20.0)
+    gcodes, out, _ = gpu_path(q, k, v, seqlens)
+    ocodes, (ref, mag), _ = oracle_path(q, k, v, seqlens)
+    for gc, oc in zip(gcodes, ocodes):
+        assert np.array_equal(codes(gc), oc)
+    assert_attn_close(bf16_to_f32(out), ref, "many short sequences", mag=mag)
+
+
 def test_distinct_tensor_scales():
     """Very different Q, K, V ranges: the three scales must each go to the right place."""
     seqlens = [200, 77]
