@@ -91,6 +91,30 @@ def test_many_short_sequences():
     assert_attn_close(bf16_to_f32(out), ref, "many short sequences", mag=mag)
 
 
+def test_max_heads():
+    """The largest head count the ABI accepts (65536: a 128-row tile of one
+    head then spans just under 2^31 bytes in the buffer descriptors), with
+    sequences of 2 and 1 tokens.  The oracle derives the scales from the full
+    tensors; codes and outputs are compared on a sample of heads (the first
+    and last 256 and 512 drawn at random)."""
+    seqlens, H = [2, 1], 65536
+    log(f"seqlens={seqlens} H={H}")
+    q, k, v = random_qkv(seqlens, H, seed=43, device=DEV, sigma=1.5)
+    gcodes, out, st = gpu_path(q, k, v, seqlens)
+    qh, kh, vh = (bf16_to_f32(t) for t in (q, k, v))
+    ost = oracle.ScaleState()
+    descale, inv = ost.forward_dynamic(np.array([oracle.amax(x) for x in (qh, kh, vh)], dtype=np.float32))
+    assert np.array_equal(np.array(qfa.read_scale_state(st)["descale"], dtype=np.float32), descale)
+    heads = np.unique(np.concatenate([np.arange(256), np.arange(H - 256, H),
+                                      np.random.default_rng(43).integers(0, H, size=512)]))
+    ocodes = [oracle.quantize(x[:, heads], inv[t]) for t, x in enumerate((qh, kh, vh))]
+    for g, o in zip(gcodes, ocodes):
+        assert np.array_equal(codes(g)[:, heads], o)
+    cu = np.concatenate([[0], np.cumsum(seqlens)])
+    ref, mag = oracle.attention(*ocodes, descale, cu, magnitude=True)
+    assert_attn_close(bf16_to_f32(out)[:, heads], ref, f"{H} heads", mag=mag)
+
+
 def test_distinct_tensor_scales():
     """Very different Q, K, V ranges: the three scales must each go to the right place."""
     seqlens = [200, 77]
