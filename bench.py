@@ -139,7 +139,7 @@ def all_configs(steps, warmup, prewarm_s):
         torch.cuda.empty_cache()
 
 
-def packed_path(head_dim, steps, warmup):
+def packed_path(head_dim, steps, warmup, prewarm_s):
     """Fused QKV projection output -> padded codes -> attention, at 1 x 8192 tokens, 16 heads of head_dim dims.
 
     Compared with what the unfused path has to do first: split Q, K, V out of the projection output and pad
@@ -167,6 +167,7 @@ def packed_path(head_dim, steps, warmup):
     sc = qfa.descale(st)
 
     def timed(fn, n):
+        prewarm(fn, prewarm_s)   # clocks settle before each loop, as for the main benchmark
         for i in range(warmup):
             fn(i)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -375,7 +376,7 @@ def main():
         all_configs(args.steps, args.warmup, args.prewarm_s)
         return
     if args.packed_head_dim:
-        packed_path(args.packed_head_dim, args.steps, args.warmup)
+        packed_path(args.packed_head_dim, args.steps, args.warmup, args.prewarm_s)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "the path runs on one GPU (sharding across GPUs is a design only); --gpus must be 1"}))
