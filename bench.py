@@ -234,6 +234,7 @@ def graph_overhead(steps):
                 qfa.fp8_varlen_attn(q8, k8, v8, sc, cu, H, out=out)
 
             def timed(fn, n):
+                prewarm(lambda i: fn(), 0.1)   # clocks settle before each loop
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 torch.cuda.synchronize()
                 e0.record(stream)
