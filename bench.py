@@ -473,7 +473,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)",
+        "dtype": "fp8_e4m3 codes (products on bf16 MFMA, fp32 accumulate, bf16 out)",
         "data": "synthetic (seeded bf16 Q/K/V, per-head sigma~U(0.5,3), 0.1% x20 outliers)",
         "config": {"workload": w.name, "seqlens": list(w.seqlens), "num_heads": H, "head_dim": 128,
                    "scaling_mode": "dynamic", "history_len": 16, "input_sets": len(sets)},
