@@ -51,6 +51,23 @@ def _run(cmd, verbose):
         print("\n".join(lines), flush=True)
 
 
+# Test infrastructure built alongside the library: a one-wave probe of the
+# matrix instructions' summation (tests/test_gpu_mfma_hw.py loads it).
+PROBE_SRC = os.path.join(ROOT, "tests", "hw", "mfma_probe.hip")
+PROBE_LIB = os.path.join(ROOT, "tests", "hw", "libmfma_probe.so")
+
+
+def build_probe(verbose: bool = True) -> str:
+    """Compile the test-side MFMA probe library; return its path."""
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="qfa_probe_") as tmp:
+        out = os.path.join(tmp, "libmfma_probe.so")
+        _run([cc, *HIPCC_FLAGS, "-shared", PROBE_SRC, "-o", out], verbose)
+        shutil.copyfile(out, PROBE_LIB + ".tmp")
+        os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
+    return PROBE_LIB
+
+
 def build(verbose: bool = True) -> str:
     """Compile every source and link the shared library; return its path."""
     cc = hipcc()
@@ -69,3 +86,4 @@ def build(verbose: bool = True) -> str:
 
 if __name__ == "__main__":
     build(verbose="-q" not in sys.argv)
+    build_probe(verbose="-q" not in sys.argv)

@@ -26,8 +26,8 @@
 //     to LDS without registers) into one staging buffer each; rows past the
 //     end of the sequence are outside the buffer descriptor's range and
 //     arrive as zeros (their scores are masked).  Once per tile, a wave group
-//     converts the codes exactly to bf16 right after one of its P V products
-//     (every E4M3 value is a bf16 value) into double-buffered bf16 tiles:
+//     converts the codes exactly to fp16 right after one of its P V products
+//     (every E4M3 value is an fp16 value) into double-buffered fp16 tiles:
 //     K in the layout of the BF16 baseline kernel (attn_common.h), V
 //     transposed (V^T, read by transposed 8-bit LDS reads of the staged
 //     codes), so that both products read their LDS operands with
@@ -40,27 +40,29 @@
 // products, in the slot of the other group's softmax head:
 //            slot 1          slot 2            slot 3          slot 4
 //   A    S_t = K_t Q^T    p_t (head)        p_t (tail)      O += P_t V_t,
-//                                                           K_{t+1} -> bf16
+//                                                           K_{t+1} -> fp16
 //   B    p_{t-1} (tail)   O += P V_{t-1},   S_t = K_t Q^T   p_t (head)
-//                         V_t -> bf16 V^T
+//                         V_t -> fp16 V^T
 //
-//   S = K Q^T       bf16 MFMA on the exactly converted codes.  gfx950's fp8
+//   S = K Q^T       fp16 MFMA on the exactly converted codes.  gfx950's fp8
 //                   MFMAs add each group of 8 products on a window of about
 //                   13 bits below the group's largest product and truncate
 //                   the rest; with outlier-heavy Q/K that moves dominant
-//                   logits by up to ~0.5 log2 units.  The bf16 MFMA sums
-//                   exactly.  The accumulator gives every lane 32 keys of ONE
+//                   logits by up to ~0.5 log2 units.  The fp16 MFMA sums
+//                   products of two E4M3 values (at most 8 significant bits)
+//                   in fp32.  The accumulator gives every lane 32 keys of ONE
 //                   query, so the row max is in-lane plus two lane swaps.
 //   online softmax  p = 2^(S c + 8 - m c), c = s_q s_k log2(e) / sqrt(D), m
 //                   a running row max that only moves when a tile's max
 //                   exceeds it by more than 0.5 log2 units (most tiles skip
 //                   the rescale).
-//   O^T += V^T P^T  bf16 MFMA: A = V^T read with ds_read_b128 from the
+//   O^T += V^T P^T  fp16 MFMA: A = V^T read with ds_read_b128 from the
 //                   converted V^T, B = P^T straight from the S accumulator
-//                   layout, rounded to bf16.  Two E4M3 terms of p (hi + lo)
+//                   layout, rounded to fp16 (11 significant bits; bf16's 8
+//                   cost up to 2^-9 of each weight).  Two E4M3 terms of p (hi + lo)
 //                   on the fp8 MFMA would cost the same matrix time plus two
 //                   slow conversions per pair of p; one E4M3 term is too
-//                   coarse.  l is the row sum of the same bf16 p, taken by an
+//                   coarse.  l is the row sum of the same fp16 p, taken by an
 //                   MFMA with an all-ones A operand (8 per tile, in the
 //                   LDS-bound P V slot, instead of 64 fp32 adds in the VALU
 //                   slot), so O / l is a convex combination of V rows.
@@ -75,7 +77,7 @@ namespace {
 
 using namespace attn;
 
-// LDS map (bytes): two bf16 K tiles | two bf16 V^T tiles | K code staging |
+// LDS map (bytes): two fp16 K tiles | two fp16 V^T tiles | K code staging |
 // V code staging = 160 KiB.
 constexpr int kCodeTile = kBN * kD;   // 16 KiB of E4M3 codes
 constexpr int kLdsK = 0;
@@ -91,15 +93,16 @@ static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 // the P^T operands.
 constexpr int kSplit = 4;
 
-// Four E4M3 codes (one dword) -> four bf16 values, exactly (scale 1).
-__device__ inline bf16x4 codes_to_bf16(uint32_t w) {
-    const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, false);
-    const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, true);
-    return bf16x4{lo[0], lo[1], hi[0], hi[1]};
+// Four E4M3 codes (one dword) -> four fp16 values, exactly (scale 1): every
+// E4M3 value (3 mantissa bits, magnitudes 2^-9 .. 448) is an fp16 normal.
+__device__ inline f16x4 codes_to_f16(uint32_t w) {
+    const f16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, false);
+    const f16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, true);
+    return f16x4{lo[0], lo[1], hi[0], hi[1]};
 }
-__device__ inline bf16x8 codes_to_bf16x8(uint32_t w0, uint32_t w1) {
-    const bf16x4 a = codes_to_bf16(w0), b = codes_to_bf16(w1);
-    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+__device__ inline f16x8 codes_to_f16x8(uint32_t w0, uint32_t w1) {
+    const f16x4 a = codes_to_f16(w0), b = codes_to_f16(w1);
+    return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
 // Asynchronous fetch of one 128-key tile of codes into a staging buffer
@@ -124,11 +127,11 @@ __device__ inline void issue_code_tile_load(const uint8_t* __restrict__ src, uin
     }
 }
 
-// Staged K codes -> one bf16 K tile, by the 256 threads of one wave group.
+// Staged K codes -> one fp16 K tile, by the 256 threads of one wave group.
 // Each 16-lane group converts the rows 2m and 2m + 1 (m = (u >> 4) + 16r,
 // r = 0..3): lanes 0..3 take 16-code chunks j = 0..3 of row 2m, lanes 4..7
 // the same chunks of row 2m + 1, lanes 8..15 chunks 4..7 of both, and each
-// chunk becomes logical bf16 chunks 2j and 2j + 1 of its row, stored at
+// chunk becomes logical fp16 chunks 2j and 2j + 1 of its row, stored at
 // chunk ^ swz_k(row).  The K staging holds chunk q of row k at q ^ 4 (k & 1)
 // (async-load lane offsets), so every group of 8 lanes reads 8 distinct
 // 16-byte slots of a 128-byte window and stores to 8 distinct chunks modulo
@@ -144,13 +147,13 @@ __device__ __forceinline__ void convert_k_tile(const unsigned char* src, unsigne
     for (int r = 0; r < 4; ++r) w[r] = *(const u32x4*)(src + rd + r * 32 * kD);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        *(bf16x8*)(d + r * 32 * kRow + 16 * ((2 * j) ^ swz)) = codes_to_bf16x8(w[r][0], w[r][1]);
-        *(bf16x8*)(d + r * 32 * kRow + 16 * ((2 * j + 1) ^ swz)) = codes_to_bf16x8(w[r][2], w[r][3]);
+        *(f16x8*)(d + r * 32 * kRow + 16 * ((2 * j) ^ swz)) = codes_to_f16x8(w[r][0], w[r][1]);
+        *(f16x8*)(d + r * 32 * kRow + 16 * ((2 * j + 1) ^ swz)) = codes_to_f16x8(w[r][2], w[r][3]);
     }
 }
 
 // ---- V^T tiles ----
-// The converted V is stored transposed, as V^T [128 dims][128 keys] bf16 in
+// The converted V is stored transposed, as V^T [128 dims][128 keys] fp16 in
 // 256-byte rows, so that P V reads its A operand with ds_read_b128 like
 // Q K^T does (half the LDS instructions of transposed 8-byte reads).  Within
 // each 32-key chunk j the keys are permuted into the order of the P^T
@@ -195,7 +198,7 @@ __device__ __forceinline__ void convert_vt(const unsigned char* src, unsigned ch
             (__attribute__((address_space(3))) v2i*)(lds_u8*)(src + (src_off ^ (uint32_t)(n << 4))));
 #pragma unroll
     for (int n = 0; n < 8; ++n)
-        *(bf16x8*)(dst + dst_off + n * 16 * kRow) = codes_to_bf16x8((uint32_t)x[n][0], (uint32_t)x[n][1]);
+        *(f16x8*)(dst + dst_off + n * 16 * kRow) = codes_to_f16x8((uint32_t)x[n][0], (uint32_t)x[n][1]);
 }
 
 // O^T += V^T P^T for one key tile over the first kDB 16-dim blocks, V^T read
@@ -204,14 +207,14 @@ __device__ __forceinline__ void convert_vt(const unsigned char* src, unsigned ch
 // block).  Each operand is requested three steps before its MFMAs issue (the
 // scheduling fence keeps it there), so LDS latency overlaps the matrix work.
 template <int kDB>
-__device__ __forceinline__ void pv_tile_t(const unsigned char* vtbase, uint32_t vt_rd, const bf16x8 (&pop)[kQB][4],
+__device__ __forceinline__ void pv_tile_t(const unsigned char* vtbase, uint32_t vt_rd, const f16x8 (&pop)[kQB][4],
                                           v4f (&o)[8][kQB]) {
     constexpr int kSteps = 4 * kDB;   // step n: dim block n >> 2, key chunk n & 3
     constexpr int kAhead = 3;
     auto operand = [&](int n) {
-        return *(const bf16x8*)(vtbase + (vt_rd ^ (uint32_t)((n & 3) << 6)) + (n >> 2) * 16 * kRow);
+        return *(const f16x8*)(vtbase + (vt_rd ^ (uint32_t)((n & 3) << 6)) + (n >> 2) * 16 * kRow);
     };
-    bf16x8 vop[4];
+    f16x8 vop[4];
 #pragma unroll
     for (int n = 0; n < kAhead; ++n) vop[n] = operand(n);
 #pragma unroll
@@ -219,32 +222,35 @@ __device__ __forceinline__ void pv_tile_t(const unsigned char* vtbase, uint32_t 
         if (n + kAhead < kSteps) vop[(n + kAhead) & 3] = operand(n + kAhead);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) o[n >> 2][qb] = mfma_bf16(vop[n & 3], pop[qb][n & 3], o[n >> 2][qb]);
+        for (int qb = 0; qb < kQB; ++qb) o[n >> 2][qb] = mfma16(vop[n & 3], pop[qb][n & 3], o[n >> 2][qb]);
     }
 }
 
-// P^T operands from p (see pack_tile, without the fp32 row sum).
-__device__ __forceinline__ void pack_bf16(const v4f (&p)[8][kQB], bf16x8 (&pop)[kQB][4]) {
+// P^T operands from p, rounded to fp16 (nearest even, v_cvt_pk_f16_f32):
+// pop[qb][j] holds p of keys 32j + 4g + i (elements 0..3) and
+// 32j + 16 + 4g + i (elements 4..7) of query r16.  p <= 2^(8 + slack) fits
+// fp16's range; 11 significant bits against bf16's 8.
+__device__ __forceinline__ void pack_f16(const v4f (&p)[8][kQB], f16x8 (&pop)[kQB][4]) {
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const v4f a = p[2 * j][qb], b = p[2 * j + 1][qb];
-            pop[qb][j] = bf16x8{(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3],
-                                (__bf16)b[0], (__bf16)b[1], (__bf16)b[2], (__bf16)b[3]};
+            pop[qb][j] = f16x8{(_Float16)a[0], (_Float16)a[1], (_Float16)a[2], (_Float16)a[3],
+                               (_Float16)b[0], (_Float16)b[1], (_Float16)b[2], (_Float16)b[3]};
         }
 }
 
-// l += the tile's row sums of the bf16 p: with every A entry 1, each output
+// l += the tile's row sums of the fp16 p: with every A entry 1, each output
 // entry of a 16x16x32 product is the sum of its query's 32 p, already
 // reduced over the lanes.
-__device__ __forceinline__ void row_sums(const bf16x8 (&pop)[kQB][4], v4f (&l)[kQB]) {
-    const __bf16 one = (__bf16)1.0f;
-    const bf16x8 ones = {one, one, one, one, one, one, one, one};
+__device__ __forceinline__ void row_sums(const f16x8 (&pop)[kQB][4], v4f (&l)[kQB]) {
+    const _Float16 one = (_Float16)1.0f;
+    const f16x8 ones = {one, one, one, one, one, one, one, one};
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) l[qb] = mfma_bf16(ones, pop[qb][j], l[qb]);
+        for (int qb = 0; qb < kQB; ++qb) l[qb] = mfma16(ones, pop[qb][j], l[qb]);
 }
 
 // Everything one wave carries through the key loop.  Lane (r16, g) of a
@@ -260,14 +266,14 @@ struct Wave {
     uint32_t row_stride;   // bytes between tokens of one head (uniform)
     int h, seq_lo, seq_hi, nt, nk_last, wave;
     float cexp;            // s_q s_k log2(e) / sqrt(D)
-    uint32_t k_rd, vt_rd;  // operand offsets inside a bf16 K / V^T tile
+    uint32_t k_rd, vt_rd;  // operand offsets inside an fp16 K / V^T tile
     uint32_t g_ld, g_ldv;  // async loads of K / V codes: row-in-segment * stride + 16-byte chunk
     uint32_t cv;           // conversion: thread index inside its group
     int g4;                // 4 g: first key row of this lane inside a 16-key block
-    bf16x8 q[kQB][4];      // Q operand (B of S = K Q^T)
+    f16x8 q[kQB][4];       // Q operand (B of S = K Q^T)
     float m[kQB];          // running row max of the raw scores (lags by <= slack / c)
     v4f o[8][kQB];         // O^T blocks [d block][query block]
-    v4f l[kQB];            // running row sums of the bf16 p per query (the 4 entries are equal)
+    v4f l[kQB];            // running row sums of the fp16 p per query (the 4 entries are equal)
 
     __device__ __forceinline__ void load_k8(lds_u8* lds, int t) const {
         issue_code_tile_load(k8, row_stride, h, seq_lo + t * kBN, seq_hi, lds + kLdsK8, wave, g_ld);
@@ -288,8 +294,8 @@ struct Wave {
 // of K_{t+1} into the K staging buffer at slot 1 (landing by the end of
 // slot 2, converted by A at slot 4), codes of V_{t+1} into the V staging
 // buffer at slot 3 (landing by the end of slot 4, converted by B at slot 2
-// of period t+1).  Buffer lifetimes: bf16 K_t is read in slots 1 (A) and 3
-// (B) of period t and rewritten with K_{t+2} at slot 4 of period t+1; bf16
+// of period t+1).  Buffer lifetimes: fp16 K_t is read in slots 1 (A) and 3
+// (B) of period t and rewritten with K_{t+2} at slot 4 of period t+1; fp16
 // V^T_t is written at slot 2 of period t, read in slot 4 of period t (A) and
 // slot 2 of period t+1 (B, which writes V^T_{t+1} into the other buffer in
 // the same slot), and rewritten with V^T_{t+2} at slot 2 of period t+2; each
@@ -299,7 +305,7 @@ __device__ __forceinline__ void key_loop(Wave<kDB>& w, unsigned char* smem) {
     lds_u8* const lds = (lds_u8*)smem;
     const int nt = w.nt;
     v4f s[8][kQB];
-    bf16x8 pop[kQB][4];
+    f16x8 pop[kQB][4];
     for (int t = 0; t <= nt; ++t) {
         const int cur = t & 1, prev = cur ^ 1;
         const int nk_t = (t + 1 < nt) ? kBN : w.nk_last;   // valid keys of tile t (t < nt)
@@ -315,7 +321,7 @@ __device__ __forceinline__ void key_loop(Wave<kDB>& w, unsigned char* smem) {
         } else {
             if (t >= 1) {
                 exp_blocks<kSplit, 8>(w, s, nk_p);
-                pack_bf16(s, pop);
+                pack_f16(s, pop);
             }
         }
         __syncthreads();
@@ -338,7 +344,7 @@ __device__ __forceinline__ void key_loop(Wave<kDB>& w, unsigned char* smem) {
         if constexpr (!kB) {
             if (t < nt) {
                 exp_blocks<kSplit, 8>(w, s, nk_t);
-                pack_bf16(s, pop);
+                pack_f16(s, pop);
             }
         } else {
             if (t < nt) {
@@ -413,7 +419,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     w.load_k8(lds, 0);
     w.load_v8(lds, 0);
 
-    // Q operand (B of S = K Q^T, bf16 16x16x32): for the c-th MFMA, lane
+    // Q operand (B of S = K Q^T, fp16 16x16x32): for the c-th MFMA, lane
     // holds query r16 of the block and head dims 32c + 8g .. + 7, the
     // mapping the K operand uses.
 #pragma unroll
@@ -423,7 +429,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
         for (int c = 0; c < kDC; ++c) {
             u32x2 a = {0, 0};
             if (qi < seq_hi) a = *(const u32x2*)(q8 + (size_t)qi * w.row_stride + (size_t)h * kD + 32 * c + 8 * g);
-            w.q[qb][c] = codes_to_bf16x8(a[0], a[1]);
+            w.q[qb][c] = codes_to_f16x8(a[0], a[1]);
         }
     }
     const float s_q = scales[0], s_k = scales[1], s_v = scales[2];

@@ -21,6 +21,9 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 constexpr int kD = 128;             // head_dim
@@ -38,8 +41,13 @@ constexpr float kMInit = -1e30f;                 // finite "no max yet", so c = 
 // Buffer descriptor word 3 for raw byte addressing on gfx9-family GPUs.
 constexpr int kRsrcWord3 = 0x00020000;
 
-__device__ inline v4f mfma_bf16(bf16x8 a, bf16x8 b, v4f c) {
+// 16x16x32 products with fp32 accumulation: bf16 operands (the BF16 kernel)
+// or fp16 operands (the E4M3 kernel, whose codes are all exact in fp16).
+__device__ inline v4f mfma16(bf16x8 a, bf16x8 b, v4f c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ inline v4f mfma16(f16x8 a, f16x8 b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 // Maximum over the four lanes {l, l^16, l^32, l^48} that hold one query.
@@ -157,10 +165,10 @@ __device__ __forceinline__ void softmax_head(W& w, v4f (&s)[8][kQB], int nk) {
     exp_blocks<0, kSplit>(w, s, nk);
 }
 
-// ---- bf16 operand tiles in LDS (both kernels run QK^T and P V on bf16) ----
+// ---- 16-bit operand tiles in LDS (bf16 in the BF16 kernel, fp16 in the E4M3 kernel) ----
 //
 // A K tile (both kernels) or V tile (BF16 kernel) is [128 keys][128 dims]
-// bf16: rows of 256 B, 16 chunks of 16 B; logical chunk c of row r sits at
+// 16-bit values: rows of 256 B, 16 chunks of 16 B; logical chunk c of row r sits at
 // chunk c ^ swz(r).
 //   K (A operand of S = K Q^T, ds_read_b128): 16 lanes read rows r..r+15 of
 //     one logical chunk; swz_k(r) = r & 15 spreads them over all 16 chunk
@@ -203,15 +211,15 @@ __device__ __forceinline__ void mfma_phase_end() { __builtin_amdgcn_s_setprio(0)
 // n / kDC, chunk n % kDC) into both query blocks; each operand is requested
 // six steps before its MFMAs issue (the scheduling fence keeps it there), so
 // a wave keeps six 1 KiB LDS reads in flight behind its matrix work.
-template <int kDC = 4>
-__device__ __forceinline__ void qk_tile(const unsigned char* kbase, uint32_t k_rd, const bf16x8 (&q)[kQB][4],
+template <int kDC = 4, class T>
+__device__ __forceinline__ void qk_tile(const unsigned char* kbase, uint32_t k_rd, const T (&q)[kQB][4],
                                         v4f (&s)[8][kQB]) {
     constexpr int kSteps = 8 * kDC;
     constexpr int kAhead = 6;
     auto operand = [&](int n) {
-        return *(const bf16x8*)(kbase + (k_rd ^ (uint32_t)((n % kDC) << 6)) + (n / kDC) * 16 * kRow);
+        return *(const T*)(kbase + (k_rd ^ (uint32_t)((n % kDC) << 6)) + (n / kDC) * 16 * kRow);
     };
-    bf16x8 kop[8];
+    T kop[8];
 #pragma unroll
     for (int n = 0; n < kAhead; ++n) kop[n] = operand(n);
 #pragma unroll
@@ -221,7 +229,7 @@ __device__ __forceinline__ void qk_tile(const unsigned char* kbase, uint32_t k_r
         const int kb = n / kDC, c = n % kDC;
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb)
-            s[kb][qb] = mfma_bf16(kop[n & 7], q[qb][c], c == 0 ? v4f{0, 0, 0, 0} : s[kb][qb]);
+            s[kb][qb] = mfma16(kop[n & 7], q[qb][c], c == 0 ? v4f{0, 0, 0, 0} : s[kb][qb]);
     }
 }
 
@@ -273,7 +281,7 @@ __device__ __forceinline__ void pv_tile(const unsigned char* vbase, uint32_t v_r
         for (int j = 0; j < 4; ++j) {
             const bf16x8 vop = read_vt(vbase, v_rd, db, j);
 #pragma unroll
-            for (int qb = 0; qb < kQB; ++qb) o[db][qb] = mfma_bf16(vop, pop[qb][j], o[db][qb]);
+            for (int qb = 0; qb < kQB; ++qb) o[db][qb] = mfma16(vop, pop[qb][j], o[db][qb]);
         }
     }
 }

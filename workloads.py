@@ -40,7 +40,7 @@ class Workload:
     outlier_scale: float
     modes: tuple             # scaling modes this workload runs
     forwards: int            # forwards per mode
-    oracle_rows: tuple = field(default=())   # (start, stop) row ranges checked at full size; () = all rows
+    oracle_rows: tuple = field(default=())   # (start, stop) row ranges checked in full at full size; () = all rows
 
     @property
     def total_tokens(self) -> int:
@@ -73,7 +73,7 @@ WORKLOADS = {
                 0.001, 20.0, ("dynamic",), 16),
     4: Workload(4, "QHD packed batch, 3x14400 tokens (90x160 patches), 16 heads", (14400, 14400, 14400), 16,
                 "per_head", "unit", 0.0, 1.0, ("dynamic", "static"), 3,
-                oracle_rows=((0, 2048), (14400 + 12352, 28800), (28800, 28800 + 2048))),
+                oracle_rows=((0, 14400), (14400 + 12352, 28800), (28800, 28800 + 2048))),
     5: Workload(5, "4K packed ragged batch, 3x32400 + 2304 tokens, 16 heads", (32400, 32400, 32400, 2304), 16,
                 "per_head", "per_head", 0.001, 20.0, ("dynamic",), 16,
                 oracle_rows=((97200, 99504), (60704, 64800))),
