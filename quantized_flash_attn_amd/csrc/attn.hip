@@ -52,10 +52,11 @@
 //                   products of two E4M3 values (at most 8 significant bits)
 //                   in fp32.  The accumulator gives every lane 32 keys of ONE
 //                   query, so the row max is in-lane plus two lane swaps.
-//   online softmax  p = 2^(S c + 8 - m c), c = s_q s_k log2(e) / sqrt(D), m
-//                   a running row max that only moves when a tile's max
-//                   exceeds it by more than 0.5 log2 units (most tiles skip
-//                   the rescale).
+//   online softmax  p = 2^(S c + 8 - mc), c = s_q s_k log2(e) / sqrt(D), mc
+//                   a running row max (log2 units) that may lag a tile's
+//                   max by 7.5 units and, when it must move, moves 3.5 units
+//                   above it; the decision is taken per 16-query block, so
+//                   most blocks skip the O and l rescale on most tiles.
 //   O^T += V^T P^T  fp16 MFMA: A = V^T read with ds_read_b128 from the
 //                   converted V^T, B = P^T straight from the S accumulator
 //                   layout, rounded to fp16 (11 significant bits; bf16's 8
@@ -271,7 +272,7 @@ struct Wave {
     uint32_t cv;           // conversion: thread index inside its group
     int g4;                // 4 g: first key row of this lane inside a 16-key block
     f16x8 q[kQB][4];       // Q operand (B of S = K Q^T)
-    float m[kQB];          // running row max of the raw scores (lags by <= slack / c)
+    float mc[kQB];         // running row max in log2 units (S c), within the rescale slack of the true max
     v4f o[8][kQB];         // O^T blocks [d block][query block]
     v4f l[kQB];            // running row sums of the fp16 p per query (the 4 entries are equal)
 
@@ -439,7 +440,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
 #pragma unroll
         for (int db = 0; db < kDB; ++db) w.o[db][qb] = v4f{0, 0, 0, 0};
         w.l[qb] = v4f{0, 0, 0, 0};
-        w.m[qb] = kMInit;
+        w.mc[qb] = kMInit;
     }
 
     wait_async_loads();

@@ -71,7 +71,7 @@ struct Wave {
     uint32_t g_k[4], g_v[4];  // async loads: row-in-segment * stride + swizzled 16-byte chunk, per segment
     int g4;                // 4 g: first key row of this lane inside a 16-key block
     bf16x8 q[kQB][4];      // Q operand (B of S = K Q^T)
-    float m[kQB];          // running row max of the scores (lags by <= slack / c)
+    float mc[kQB];         // running row max in log2 units (S c), within the rescale slack of the true max
     v4f o[8][kQB];         // O^T blocks [d block][query block]
     float l[kQB];          // running sum of p over the keys this lane holds (reduced over the quad at the end)
 
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_fwd_kernel(
 #pragma unroll
         for (int db = 0; db < 8; ++db) w.o[db][qb] = v4f{0, 0, 0, 0};
         w.l[qb] = 0.0f;
-        w.m[qb] = kMInit;
+        w.mc[qb] = kMInit;
     }
 
     wait_async_loads();

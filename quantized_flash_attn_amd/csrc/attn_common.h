@@ -35,8 +35,16 @@ constexpr int kBM = kWaves * kQB * 16;  // 256 queries per workgroup
 constexpr int kBN = 128;            // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRsqrtD = 0.08838834764831845f;  // 1/sqrt(128)
-constexpr float kRescaleSlack = 0.5f;            // log2 units the running max may lag
-constexpr float kMInit = -1e30f;                 // finite "no max yet", so c = 0 gives no NaN
+// Rescale policy of the online softmax.  p = 2^(S c + 8 - mc), with mc the
+// running row max in log2 units, is rounded to fp16 (bf16 in the BF16
+// kernel) for P V.  mc may lag a tile's max by up to kRescaleSlack units, so
+// p <= 2^15.5 stays below fp16's largest value (65504 ~= 2^16); when a
+// tile's max exceeds it by more, mc moves kRescaleHeadroom units above that
+// max, so the next 11 units of growth need no rescale while the largest p of
+// the row stays >= 2^4.5, far from fp16's subnormal range (2^-14).
+constexpr float kRescaleSlack = 7.5f;
+constexpr float kRescaleHeadroom = 3.5f;
+constexpr float kMInit = -1e30f;                 // finite "no max yet": every first tile rescales, to 0 * O
 
 // Buffer descriptor word 3 for raw byte addressing on gfx9-family GPUs.
 constexpr int kRsrcWord3 = 0x00020000;
@@ -101,7 +109,7 @@ template <int kLo, int kHi, class W>
 __device__ __forceinline__ void exp_blocks(const W& w, v4f (&s)[8][kQB], int nk) {
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
-        const float bias = 8.0f - w.m[qb] * w.cexp;
+        const float bias = 8.0f - w.mc[qb];
 #pragma unroll
         for (int kb = kLo; kb < kHi; ++kb)
 #pragma unroll
@@ -121,13 +129,15 @@ __device__ __forceinline__ void exp_blocks(const W& w, v4f (&s)[8][kQB], int nk)
 }
 
 // Online-softmax step for one key tile with nk valid keys, first part:
-// mask the keys past nk, take the row max, and, if it exceeds the running
-// max m by more than the slack anywhere in the wave, move m to it for every
-// query and rescale O and l (which hold the earlier tiles).  Then turn the
-// scores of key blocks [0, kSplit) into p = 2^(S c + 8 - m c); the rest
-// follow with exp_blocks<kSplit, 8>.  s[kb][qb] holds keys 16kb + 4g + i of
-// query r16 (lane (r16, g), g4 = 4g).  W carries m[kQB], l[kQB],
-// o[8][kQB] (of which the first W::kDB dim blocks are live), cexp and g4.
+// mask the keys past nk and take each query's tile max tm (log2 units).  For
+// each 16-query block separately: if tm exceeds the running max mc by more
+// than the slack for any of its queries, move mc to max(mc, tm + headroom)
+// for each of them and rescale that block's O and l (which hold the earlier
+// tiles) by 2^(mc_old - mc_new).  Then turn the scores of key blocks
+// [0, kSplit) into p = 2^(S c + 8 - mc); the rest follow with
+// exp_blocks<kSplit, 8>.  s[kb][qb] holds keys 16kb + 4g + i of query r16
+// (lane (r16, g), g4 = 4g).  W carries mc[kQB], l[kQB], o[8][kQB] (of which
+// the first W::kDB dim blocks are live), cexp and g4.
 template <int kSplit, class W>
 __device__ __forceinline__ void softmax_head(W& w, v4f (&s)[8][kQB], int nk) {
     if (nk < kBN) {
@@ -140,8 +150,6 @@ __device__ __forceinline__ void softmax_head(W& w, v4f (&s)[8][kQB], int nk) {
                 for (int qb = 0; qb < kQB; ++qb) s[kb][qb][i] = dead ? -INFINITY : s[kb][qb][i];
             }
     }
-    float mn[kQB];
-    bool grow = false;
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
         float mx = s[0][qb][0];
@@ -149,14 +157,11 @@ __device__ __forceinline__ void softmax_head(W& w, v4f (&s)[8][kQB], int nk) {
         for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][qb][i]);
-        mn[qb] = fmaxf(w.m[qb], quad_max(mx));
-        grow |= (mn[qb] - w.m[qb]) * w.cexp > kRescaleSlack;
-    }
-    if (__any(grow)) {
-#pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) {
-            const float alpha = __builtin_amdgcn_exp2f((w.m[qb] - mn[qb]) * w.cexp);
-            w.m[qb] = mn[qb];
+        const float tm = quad_max(mx) * w.cexp;
+        if (__any(tm - w.mc[qb] > kRescaleSlack)) {
+            const float mc = fmaxf(w.mc[qb], tm + kRescaleHeadroom);
+            const float alpha = __builtin_amdgcn_exp2f(w.mc[qb] - mc);
+            w.mc[qb] = mc;
             w.l[qb] *= alpha;
 #pragma unroll
             for (int db = 0; db < W::kDB; ++db) w.o[db][qb] *= alpha;
