@@ -124,6 +124,17 @@ def all_configs(steps, warmup, prewarm_s):
         ms_q = timed(lambda i: qfa.quantize_qkv(st, mode, *sets[i % n_sets], *codes[i % n_sets]), n)
         ms_a = timed(lambda i: qfa.fp8_varlen_attn(*codes[i % n_sets], scs[i % n_sets], cu, H, out=out), n)
         ms_b = timed(lambda i: qfa.bf16_varlen_attn(*sets[i % n_sets], cu, H, out=out), n)
+        # the split-key launch where the automatic count splits (small images), on a workspace allocated once
+        splits = qfa.fp8_varlen_attn_auto_splits(len(w.seqlens), T, H)
+        split = None
+        if splits > 1:
+            ws = torch.empty(qfa.fp8_varlen_attn_workspace_bytes(len(w.seqlens), T, H, splits), dtype=torch.uint8,
+                             device=dev)
+            ms_s = timed(lambda i: qfa.fp8_varlen_attn_split(*codes[i % n_sets], scs[i % n_sets], cu, H,
+                                                             num_splits=splits, workspace=ws, out=out), n)
+            split = {"num_splits": splits, "ms": round(ms_s, 4), "tflops": round(w.attn_flop / (ms_s * 1e-3) / 1e12, 1),
+                     "step_incl_quant_ms": round(ms_q + ms_s, 4),
+                     "fp8_speedup_incl_quant": round(ms_b / (ms_q + ms_s), 3)}
         qbytes = 3 * 3 * T * H * 128   # read 2 B and write 1 B per element (one pass)
         flop = w.attn_flop
         print(json.dumps({"config": {
@@ -136,6 +147,7 @@ def all_configs(steps, warmup, prewarm_s):
             "step_incl_quant": {"ms": round(ms_q + ms_a, 4), "tflops": round(flop / ((ms_q + ms_a) * 1e-3) / 1e12, 1)},
             "bf16_attention": {"ms": round(ms_b, 4), "tflops": round(flop / (ms_b * 1e-3) / 1e12, 1)},
             "fp8_speedup_incl_quant": round(ms_b / (ms_q + ms_a), 3),
+            "fp8_split_attention": split,
             "launches": n}}), flush=True)
         del sets, codes, out
         torch.cuda.empty_cache()

@@ -49,7 +49,8 @@ typedef enum qfa_status {
     QFA_ERR_VALUE = 7,       /* history_len not in 1..16; static amax, margin or their product not finite and > 0 */
     QFA_ERR_STATE = 8,       /* the handle was not initialised by qfa_init_scale_state */
     QFA_ERR_HIP = 9,         /* a HIP runtime error */
-    QFA_ERR_DATA = 10        /* qfa_check_cu_seqlens found invalid cu_seqlens contents */
+    QFA_ERR_DATA = 10,       /* qfa_check_cu_seqlens found invalid cu_seqlens contents */
+    QFA_ERR_WORKSPACE = 11   /* a split launch's workspace is missing or smaller than it needs */
 } qfa_status;
 
 typedef enum qfa_mode {
@@ -59,6 +60,7 @@ typedef enum qfa_mode {
 
 #define QFA_HEAD_DIM 128
 #define QFA_MAX_HISTORY 16
+#define QFA_MAX_SPLITS 16   /* key ranges per query tile in qfa_fp8_varlen_attn_split */
 
 /*
  * Host handle of one attention layer's scale state.  Filled by
@@ -176,13 +178,58 @@ const float* qfa_descale_ptr(const qfa_scale_state* st);
  *   out            device bf16 [total_tokens, num_heads, head_dim] (out)
  * total_tokens must be below 2^31 and num_heads at most 65536
  * (QFA_ERR_SHAPE otherwise).  The kernel converts the codes exactly to
- * bf16 and runs both products on bf16 MFMAs with float32 accumulation; the
- * probabilities are rounded to bf16 for the P*V product.
+ * fp16 and runs both products on fp16 MFMAs with float32 accumulation; the
+ * probabilities are rounded to fp16 for the P*V product.
  */
 qfa_status qfa_fp8_varlen_attn(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                                const float* scales, const int32_t* cu_seqlens, int num_seqs,
                                int64_t total_tokens, int num_heads, int head_dim, void* out,
                                void* stream);
+
+/*
+ * The same attention with the keys of each (head, 256-query tile) split into
+ * up to QFA_MAX_SPLITS ranges of whole 128-key tiles, one workgroup per
+ * range, for launches that would leave compute units idle (small images:
+ * "FP8 ViT Encoder Attention", Performance, finds no FP8 gain there; "FP8
+ * vision encoder attention", Expected performance, measures 2304 tokens).
+ * Each range writes, per query, its partial output normalised by its own
+ * softmax sum (fp16, in code units) plus its running max and sum (float32)
+ * to `workspace`; a second kernel merges the ranges with the usual
+ * max-shifted weights and writes `out`.  Arguments as qfa_fp8_varlen_attn,
+ * plus:
+ *   num_splits       0 = qfa_fp8_varlen_attn_auto_splits(...), else 1..16;
+ *                    1 runs qfa_fp8_varlen_attn (no workspace used).
+ *                    Ranges past a sequence's last key tile are empty.
+ *   workspace        caller-owned device memory, 16-byte aligned, of at least
+ *                    qfa_fp8_varlen_attn_workspace_bytes(...) bytes; may be
+ *                    NULL when the split count resolves to 1.  Its contents
+ *                    on entry do not matter and are garbage on return.
+ *   workspace_bytes  its size (QFA_ERR_WORKSPACE if too small or missing)
+ * QFA_ERR_VALUE for num_splits outside 0..16.  Calls sharing one workspace
+ * must be ordered on one stream.
+ */
+qfa_status qfa_fp8_varlen_attn_split(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                                     const float* scales, const int32_t* cu_seqlens, int num_seqs,
+                                     int64_t total_tokens, int num_heads, int head_dim, int num_splits,
+                                     void* workspace, size_t workspace_bytes, void* out, void* stream);
+
+/*
+ * Split count qfa_fp8_varlen_attn_split uses for num_splits = 0: as many
+ * ranges as keep every workgroup of the launch in one round of the 256
+ * compute units (256-query tiles x heads x ranges <= 256), each of at least
+ * two 128-key tiles of a sequence of the batch's mean length, at most 16; 1
+ * when that is fewer than two.  (A second round of workgroups costs about
+ * what the split saves.)  Host-only, no device access.
+ */
+int qfa_fp8_varlen_attn_auto_splits(int num_seqs, int64_t total_tokens, int num_heads);
+
+/*
+ * Workspace bytes qfa_fp8_varlen_attn_split needs for num_splits (0 = the
+ * automatic count): for S > 1 ranges, S * num_heads * (total_tokens / 256 +
+ * num_seqs) * 256 query rows of 128 fp16 plus 2 float32, rounded up; 0 when
+ * the count resolves to 1 or an argument is out of range.  Host-only.
+ */
+size_t qfa_fp8_varlen_attn_workspace_bytes(int num_seqs, int64_t total_tokens, int num_heads, int num_splits);
 
 /*
  * Varlen BF16 attention, the baseline FP8 attention is compared against

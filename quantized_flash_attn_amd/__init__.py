@@ -18,6 +18,11 @@ Entry points (same names as the C ABI without the ``qfa_`` prefix):
 * ``descale(state)`` -> device float32[3] view {s_q, s_k, s_v}
 * ``fp8_varlen_attn(q8, k8, v8, scales, cu_seqlens, num_heads, head_dim=128, out=None)``:
   codes ``[T, H, 128]``; output ``[T, H, head_dim]``
+* ``fp8_varlen_attn_split(q8, k8, v8, scales, cu_seqlens, num_heads, head_dim=128, num_splits=0,
+  workspace=None, out=None)``: the same with each query tile's keys split into ranges (small images);
+  ``workspace`` is a caller-owned uint8 device tensor (allocated here when not given)
+* ``fp8_varlen_attn_auto_splits(num_seqs, total_tokens, num_heads)``,
+  ``fp8_varlen_attn_workspace_bytes(num_seqs, total_tokens, num_heads, num_splits=0)``
 * ``bf16_varlen_attn(q, k, v, cu_seqlens, num_heads, head_dim=128, out=None)`` (the BF16 baseline)
 * ``read_scale_state(state)`` -> dict (synchronises; for tests and checkpoints)
 * ``check_cu_seqlens(cu_seqlens, total_tokens)`` (synchronises)
@@ -53,6 +58,7 @@ STATUS = {
     8: "QFA_ERR_STATE",
     9: "QFA_ERR_HIP",
     10: "QFA_ERR_DATA",
+    11: "QFA_ERR_WORKSPACE",
 }
 
 
@@ -103,6 +109,10 @@ def _load():
         "qfa_quantize_qkv_packed": (i32, [ctypes.POINTER(_State), i32, vp, i64, i32, i32, vp, vp, vp, vp]),
         "qfa_descale_ptr": (vp, [ctypes.POINTER(_State)]),
         "qfa_fp8_varlen_attn": (i32, [vp, vp, vp, vp, vp, i32, i64, i32, i32, vp, vp]),
+        "qfa_fp8_varlen_attn_split": (i32, [vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, vp, ctypes.c_size_t, vp,
+                                            vp]),
+        "qfa_fp8_varlen_attn_auto_splits": (i32, [i32, i64, i32]),
+        "qfa_fp8_varlen_attn_workspace_bytes": (ctypes.c_size_t, [i32, i64, i32, i32]),
         "qfa_bf16_varlen_attn": (i32, [vp, vp, vp, vp, i32, i64, i32, i32, vp, vp]),
         "qfa_read_scale_state": (i32, [ctypes.POINTER(_State), ctypes.POINTER(_Snapshot), vp]),
         "qfa_check_cu_seqlens": (i32, [vp, i32, i64, vp]),
@@ -127,6 +137,9 @@ EXPORTS = (
     "qfa_quantize_qkv_packed",
     "qfa_descale_ptr",
     "qfa_fp8_varlen_attn",
+    "qfa_fp8_varlen_attn_split",
+    "qfa_fp8_varlen_attn_auto_splits",
+    "qfa_fp8_varlen_attn_workspace_bytes",
     "qfa_bf16_varlen_attn",
     "qfa_read_scale_state",
     "qfa_check_cu_seqlens",
@@ -261,6 +274,59 @@ def descale(state: ScaleState) -> torch.Tensor:
         raise QfaError(8, "state not initialised")
     off = ptr - state.buffer.data_ptr()
     return state.buffer[off:off + 12].view(torch.float32)
+
+
+def _attn_args(q8, k8, v8, scales, cu_seqlens, num_heads, head_dim, out):
+    _require_gpu(q8, k8, v8, scales, cu_seqlens)
+    T, H, D = _qkv_shape(q8)
+    if num_heads is not None and num_heads != H:
+        raise ValueError("num_heads does not match q8")
+    for t in (q8, k8, v8):
+        if t.dtype != torch.uint8 or tuple(t.shape) != (T, H, HEAD_DIM) or not t.is_contiguous():
+            raise ValueError("q8, k8, v8 must be contiguous uint8 tensors [tokens, heads, 128]")
+    if scales.dtype != torch.float32 or scales.numel() < 3:
+        raise ValueError("scales must be float32[3]")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be int32[num_seqs + 1]")
+    if out is None:
+        out = torch.empty((T, H, head_dim), dtype=torch.bfloat16, device=q8.device)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (T, H, head_dim) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 tensor [tokens, heads, head_dim]")
+    return T, H, out
+
+
+def fp8_varlen_attn_auto_splits(num_seqs: int, total_tokens: int, num_heads: int) -> int:
+    """Key ranges ``fp8_varlen_attn_split`` uses when ``num_splits`` is 0 (1 = no split)."""
+    return int(_lib.qfa_fp8_varlen_attn_auto_splits(int(num_seqs), int(total_tokens), int(num_heads)))
+
+
+def fp8_varlen_attn_workspace_bytes(num_seqs: int, total_tokens: int, num_heads: int, num_splits: int = 0) -> int:
+    """Workspace bytes ``fp8_varlen_attn_split`` needs (0 when the split count resolves to 1)."""
+    return int(_lib.qfa_fp8_varlen_attn_workspace_bytes(int(num_seqs), int(total_tokens), int(num_heads),
+                                                        int(num_splits)))
+
+
+def fp8_varlen_attn_split(q8, k8, v8, scales, cu_seqlens, num_heads=None, head_dim=HEAD_DIM, num_splits=0,
+                          workspace=None, out=None):
+    """``fp8_varlen_attn`` with each (head, query tile)'s keys split into ``num_splits`` ranges (0 = automatic).
+
+    ``workspace``: a contiguous uint8 device tensor of at least ``fp8_varlen_attn_workspace_bytes`` bytes; when
+    None, one is allocated here (a torch tensor, like ``out``).
+    """
+    T, H, out = _attn_args(q8, k8, v8, scales, cu_seqlens, num_heads, head_dim, out)
+    B = cu_seqlens.numel() - 1
+    need = fp8_varlen_attn_workspace_bytes(B, T, H, num_splits) if 0 <= num_splits <= 16 else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q8.device)
+    _require_gpu(workspace)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    with torch.cuda.device(q8.device):
+        _check(_lib.qfa_fp8_varlen_attn_split(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), scales.data_ptr(),
+                                              cu_seqlens.data_ptr(), B, T, H, head_dim, int(num_splits),
+                                              workspace.data_ptr(), workspace.numel(), out.data_ptr(),
+                                              _stream_ptr(q8.device)))
+    return out
 
 
 def fp8_varlen_attn(q8, k8, v8, scales, cu_seqlens, num_heads=None, head_dim=HEAD_DIM, out=None):

@@ -1,6 +1,7 @@
 // C ABI of the library: argument validation (before any HIP call), status
 // codes, thread-local error text, and dispatch to the kernel launchers.
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -52,6 +53,11 @@ qfa_status check_shape(int64_t total_tokens, int num_heads, int head_dim, int64_
     return QFA_OK;
 }
 
+// The attention kernels fetch up to 128 token rows of one head through a
+// buffer descriptor whose 32-bit range spans those rows at a stride of
+// num_heads * 256 bytes (bf16); 65536 heads keep it below 2^31.
+constexpr int kMaxAttnHeads = 65536;
+
 // Head dims the padded paths accept: 8..128 in steps of 8 (16-byte bf16 rows).
 bool padded_head_dim_ok(int head_dim) { return head_dim >= 8 && head_dim <= QFA_HEAD_DIM && head_dim % 8 == 0; }
 
@@ -74,6 +80,7 @@ const char* qfa_status_string(qfa_status s) {
         case QFA_ERR_STATE: return "scale state not initialised";
         case QFA_ERR_HIP: return "HIP runtime error";
         case QFA_ERR_DATA: return "invalid cu_seqlens contents";
+        case QFA_ERR_WORKSPACE: return "workspace missing or too small";
     }
     return "unknown status";
 }
@@ -172,30 +179,99 @@ const float* qfa_descale_ptr(const qfa_scale_state* st) {
     return ((const qfa::DeviceState*)st->device)->descale;
 }
 
-// The attention kernels fetch up to 128 token rows of one head through a
-// buffer descriptor whose 32-bit range spans those rows at a stride of
-// num_heads * 256 bytes (bf16); 65536 heads keep it below 2^31.
-constexpr int kMaxAttnHeads = 65536;
+}  // extern "C"
 
-qfa_status qfa_fp8_varlen_attn(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* scales,
-                               const int32_t* cu_seqlens, int num_seqs, int64_t total_tokens, int num_heads,
-                               int head_dim, void* out, void* stream) {
-    const char* where = "qfa_fp8_varlen_attn";
+namespace {
+
+// Checks shared by the FP8 attention entry points; *n = code elements per tensor.
+qfa_status check_fp8_attn(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* scales,
+                          const int32_t* cu_seqlens, int num_seqs, int64_t total_tokens, int num_heads, int head_dim,
+                          const void* out, int64_t* n, const char* where) {
     if (!padded_head_dim_ok(head_dim))
         return fail(QFA_ERR_UNSUPPORTED, "%s: head_dim %d (8..128 in steps of 8)", where, head_dim);
-    int64_t n = 0;
-    qfa_status s = check_shape(total_tokens, num_heads, QFA_HEAD_DIM, &n, where);  // code rows are 128 wide
+    qfa_status s = check_shape(total_tokens, num_heads, QFA_HEAD_DIM, n, where);  // code rows are 128 wide
     if (s != QFA_OK) return s;
     if (num_seqs < 1) return fail(QFA_ERR_SHAPE, "%s: num_seqs %d must be at least 1", where, num_seqs);
     if (total_tokens >= (INT64_C(1) << 31)) return fail(QFA_ERR_SHAPE, "%s: total_tokens must be below 2^31", where);
     if (num_heads > kMaxAttnHeads)
         return fail(QFA_ERR_SHAPE, "%s: num_heads %d above %d", where, num_heads, kMaxAttnHeads);
     if (!scales || !cu_seqlens) return fail(QFA_ERR_NULL, "%s: null scales or cu_seqlens", where);
-    if (n > 0 && (!q8 || !k8 || !v8 || !out)) return fail(QFA_ERR_NULL, "%s: null tensor pointer", where);
-    if (n > 0 && !(aligned16(q8) && aligned16(k8) && aligned16(v8) && aligned16(out)))
+    if (*n > 0 && (!q8 || !k8 || !v8 || !out)) return fail(QFA_ERR_NULL, "%s: null tensor pointer", where);
+    if (*n > 0 && !(aligned16(q8) && aligned16(k8) && aligned16(v8) && aligned16(out)))
         return fail(QFA_ERR_ALIGN, "%s: tensor pointer not 16-byte aligned", where);
     if (((uintptr_t)scales & 3u) || ((uintptr_t)cu_seqlens & 3u))
         return fail(QFA_ERR_ALIGN, "%s: scales / cu_seqlens not 4-byte aligned", where);
+    return QFA_OK;
+}
+
+// Key-range splits for a launch that fills few CUs.  Measured on one
+// MI355X with one workgroup per CU: a workgroup streaming n key tiles takes
+// about 2.9 n + 9.6 us when every workgroup of the launch fits in one round
+// of the 256 CUs, and a second round costs about as much as the split saves.
+// So the keys are split into as many ranges as still fit in one round, each
+// of at least two 128-key tiles of a sequence of the batch's mean length (the
+// split only matters for small batches, whose images are of similar size),
+// at most QFA_MAX_SPLITS; 1 when that is fewer than two ranges.
+int auto_splits(int num_seqs, int64_t total_tokens, int num_heads) {
+    if (total_tokens <= 0 || num_seqs < 1 || num_heads < 1) return 1;
+    const int64_t query_tiles = ((total_tokens + 255) / 256 + (num_seqs - 1)) * num_heads;
+    const int64_t mean_len = (total_tokens + num_seqs - 1) / num_seqs;
+    const int64_t nt = (mean_len + 127) / 128;
+    int64_t sp = std::min<int64_t>(256 / query_tiles, nt / 2);
+    sp = std::min<int64_t>(sp, QFA_MAX_SPLITS);
+    return sp >= 2 ? (int)sp : 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qfa_fp8_varlen_attn_auto_splits(int num_seqs, int64_t total_tokens, int num_heads) {
+    return auto_splits(num_seqs, total_tokens, num_heads);
+}
+
+size_t qfa_fp8_varlen_attn_workspace_bytes(int num_seqs, int64_t total_tokens, int num_heads, int num_splits) {
+    if (num_seqs < 1 || num_heads < 1 || total_tokens < 0 || total_tokens >= (INT64_C(1) << 31)) return 0;
+    if (num_splits < 0 || num_splits > QFA_MAX_SPLITS) return 0;
+    const int sp = num_splits == 0 ? auto_splits(num_seqs, total_tokens, num_heads) : num_splits;
+    return qfa::attention_workspace_bytes(num_seqs, (int)total_tokens, num_heads, sp);
+}
+
+qfa_status qfa_fp8_varlen_attn_split(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* scales,
+                                     const int32_t* cu_seqlens, int num_seqs, int64_t total_tokens, int num_heads,
+                                     int head_dim, int num_splits, void* workspace, size_t workspace_bytes,
+                                     void* out, void* stream) {
+    const char* where = "qfa_fp8_varlen_attn_split";
+    int64_t n = 0;
+    qfa_status s = check_fp8_attn(q8, k8, v8, scales, cu_seqlens, num_seqs, total_tokens, num_heads, head_dim, out,
+                                  &n, where);
+    if (s != QFA_OK) return s;
+    if (num_splits < 0 || num_splits > QFA_MAX_SPLITS)
+        return fail(QFA_ERR_VALUE, "%s: num_splits %d not in 0..%d", where, num_splits, QFA_MAX_SPLITS);
+    const int sp = num_splits == 0 ? auto_splits(num_seqs, total_tokens, num_heads) : num_splits;
+    const size_t need = qfa::attention_workspace_bytes(num_seqs, (int)total_tokens, num_heads, sp);
+    if (n > 0 && sp > 1) {
+        if (!workspace) return fail(QFA_ERR_WORKSPACE, "%s: %d key ranges need a workspace", where, sp);
+        if (!aligned16(workspace)) return fail(QFA_ERR_ALIGN, "%s: workspace not 16-byte aligned", where);
+        if (workspace_bytes < need)
+            return fail(QFA_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", where, workspace_bytes, need);
+    }
+    s = check_pending(where);
+    if (s != QFA_OK) return s;
+    if (n == 0) return ok();
+    const hipError_t e = qfa::launch_attention_split(q8, k8, v8, scales, cu_seqlens, num_seqs, (int)total_tokens,
+                                                     num_heads, head_dim, sp, workspace, out, (hipStream_t)stream);
+    return check_launch(e, where);
+}
+
+qfa_status qfa_fp8_varlen_attn(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* scales,
+                               const int32_t* cu_seqlens, int num_seqs, int64_t total_tokens, int num_heads,
+                               int head_dim, void* out, void* stream) {
+    const char* where = "qfa_fp8_varlen_attn";
+    int64_t n = 0;
+    qfa_status s = check_fp8_attn(q8, k8, v8, scales, cu_seqlens, num_seqs, total_tokens, num_heads, head_dim, out,
+                                  &n, where);
+    if (s != QFA_OK) return s;
     s = check_pending(where);
     if (s != QFA_OK) return s;
     if (n == 0) return ok();

@@ -54,7 +54,7 @@
 //                   query, so the row max is in-lane plus two lane swaps.
 //   online softmax  p = 2^(S c + 8 - mc), c = s_q s_k log2(e) / sqrt(D), mc
 //                   a running row max (log2 units) that may lag a tile's
-//                   max by 7.5 units and, when it must move, moves 3.5 units
+//                   max by 7.5 units and, when it must move, moves 4 units
 //                   above it; the decision is taken per 16-query block, so
 //                   most blocks skip the O and l rescale on most tiles.
 //   O^T += V^T P^T  fp16 MFMA: A = V^T read with ds_read_b128 from the
@@ -265,7 +265,7 @@ struct Wave {
     const uint8_t* k8;
     const uint8_t* v8;
     uint32_t row_stride;   // bytes between tokens of one head (uniform)
-    int h, seq_lo, seq_hi, nt, nk_last, wave;
+    int h, seq_hi, k0, nt, nk_last, wave;   // keys [k0, k0 + 128 nt) of the sequence ending at seq_hi
     float cexp;            // s_q s_k log2(e) / sqrt(D)
     uint32_t k_rd, vt_rd;  // operand offsets inside an fp16 K / V^T tile
     uint32_t g_ld, g_ldv;  // async loads of K / V codes: row-in-segment * stride + 16-byte chunk
@@ -277,10 +277,10 @@ struct Wave {
     v4f l[kQB];            // running row sums of the fp16 p per query (the 4 entries are equal)
 
     __device__ __forceinline__ void load_k8(lds_u8* lds, int t) const {
-        issue_code_tile_load(k8, row_stride, h, seq_lo + t * kBN, seq_hi, lds + kLdsK8, wave, g_ld);
+        issue_code_tile_load(k8, row_stride, h, k0 + t * kBN, seq_hi, lds + kLdsK8, wave, g_ld);
     }
     __device__ __forceinline__ void load_v8(lds_u8* lds, int t) const {
-        issue_code_tile_load(v8, row_stride, h, seq_lo + t * kBN, seq_hi, lds + kLdsV8, wave, g_ldv);
+        issue_code_tile_load(v8, row_stride, h, k0 + t * kBN, seq_hi, lds + kLdsV8, wave, g_ldv);
     }
     __device__ __forceinline__ void convert_k(unsigned char* smem, int buf) const {
         convert_k_tile(smem + kLdsK8, smem + kLdsK + buf * kTileBytes, cv);
@@ -372,34 +372,61 @@ __device__ __forceinline__ void key_loop(Wave<kDB>& w, unsigned char* smem) {
     }
 }
 
-template <int kDC, int kDB>
+// kPartial: the keys of each sequence are split into num_splits ranges of
+// whole key tiles, one workgroup per (head, query tile, range); instead of the
+// output, a workgroup writes for each of its queries the partial result over
+// its range, normalised by its own row sum and kept in code units (a convex
+// combination of V codes, so |value| <= 448 fits fp16), and (mc, l): its
+// running max in log2 units and its row sum.  attn_combine_kernel merges the
+// ranges.  Partial rows are indexed [split][head][virtual tile][query in
+// tile] and hold 128 fp16 dims (those past the live blocks unwritten).
+template <int kDC, int kDB, bool kPartial>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8, const uint8_t* __restrict__ v8,
     const float* __restrict__ scales, const int32_t* __restrict__ cu, int num_seqs, int num_heads,
-    int tiles_per_head, int head_dim, float log2e_rsqrt_d, __bf16* __restrict__ out) {
+    int tiles_per_head, int num_splits, int head_dim, float log2e_rsqrt_d, __bf16* __restrict__ out,
+    _Float16* __restrict__ part_o, v2f* __restrict__ part_ml) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
     lds_u8* const lds = (lds_u8*)smem;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int r16 = lane & 15, g = lane >> 4;
 
+    // logical id = (head, key range, virtual query tile): consecutive ids
+    // share one head's K/V range and land on one XCD
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
-    const int h = logical / tiles_per_head;
-    const int vt = logical - h * tiles_per_head;
+    const int per_head = tiles_per_head * num_splits;
+    const int h = logical / per_head;
+    const int rem = logical - h * per_head;
+    const int split = rem / tiles_per_head;
+    const int vt = rem - split * tiles_per_head;
     const int b = find_sequence(cu, num_seqs, vt);
     const int seq_lo = cu[b], seq_hi = cu[b + 1];
     const int q0 = seq_lo + (vt - (seq_lo / kBM + b)) * kBM;
     if (q0 >= seq_hi) return;  // spare tile (uniform over the workgroup)
+
+    // key tiles [t0, t0 + nt) of the sequence's nt_seq
+    const int nt_seq = (seq_hi - seq_lo + kBN - 1) / kBN;
+    const int per = (nt_seq + num_splits - 1) / num_splits;
+    const int t0 = min(nt_seq, split * per);
+    const int nt = min(nt_seq, t0 + per) - t0;
+    const size_t prow0 = ((size_t)(split * num_heads + h) * tiles_per_head + vt) * kBM;
+    if constexpr (kPartial) {
+        if (nt == 0) {   // a range past the sequence's last key tile: an empty partial (l = 0)
+            if (tid < kBM && q0 + tid < seq_hi) part_ml[prow0 + tid] = v2f{kMInit, 0.0f};
+            return;
+        }
+    }
 
     Wave<kDB> w;
     w.k8 = k8;
     w.v8 = v8;
     w.row_stride = (uint32_t)num_heads * kD;
     w.h = h;
-    w.seq_lo = seq_lo;
     w.seq_hi = seq_hi;
-    w.nt = (seq_hi - seq_lo + kBN - 1) / kBN;
-    w.nk_last = seq_hi - seq_lo - (w.nt - 1) * kBN;
+    w.k0 = seq_lo + t0 * kBN;
+    w.nt = nt;
+    w.nk_last = min(kBN, seq_hi - (w.k0 + (nt - 1) * kBN));
     w.wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in an SGPR
     const bool group_b = w.wave >= kWaves / 2;          // wave-uniform
     w.k_rd = k_operand_offset(r16, g);
@@ -463,6 +490,27 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     // ---- epilogue: lane holds O^T[d = 16db + 4g + i][query r16]; the output
     // rows hold head_dim dims (a multiple of 8, so a lane's 4 dims are all
     // inside or all past it) ----
+    if constexpr (kPartial) {
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) {
+            const int qt = w.wave * (16 * kQB) + qb * 16 + r16;   // query in tile
+            if (q0 + qt < seq_hi) {
+                const float il = 1.0f / w.l[qb][0];
+                _Float16* dst = part_o + (prow0 + qt) * kD + 4 * g;
+#pragma unroll
+                for (int db = 0; db < kDB; ++db) {
+                    f16x4 r;
+                    r[0] = (_Float16)(w.o[db][qb][0] * il);
+                    r[1] = (_Float16)(w.o[db][qb][1] * il);
+                    r[2] = (_Float16)(w.o[db][qb][2] * il);
+                    r[3] = (_Float16)(w.o[db][qb][3] * il);
+                    *(f16x4*)(dst + 16 * db) = r;
+                }
+                if (g == 0) part_ml[prow0 + qt] = v2f{w.mc[qb], w.l[qb][0]};
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
         const int qi = q0 + w.wave * (16 * kQB) + qb * 16 + r16;
@@ -484,27 +532,112 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     }
 }
 
+// Merge the key ranges of attn_fwd_kernel<.., true>.  Workgroup = 16
+// queries of one (head, virtual query tile), 16 threads per query, thread c
+// covering dims 8c .. 8c + 7, so a wave reads and writes whole rows.  With M
+// the largest range max and w_s = 2^(mc_s - M) l_s, out = bf16(s_v *
+// sum_s w_s O_s / sum_s w_s): the softmax normalisation over the whole
+// sequence.  Empty ranges (l = 0) are skipped, so their unwritten rows are
+// never read.
+constexpr int kCombineQueries = 16;   // queries per combine workgroup
+__global__ __launch_bounds__(256) void attn_combine_kernel(const _Float16* __restrict__ part_o,
+                                                           const v2f* __restrict__ part_ml,
+                                                           const float* __restrict__ scales,
+                                                           const int32_t* __restrict__ cu, int num_seqs,
+                                                           int num_heads, int tiles_per_head, int num_splits,
+                                                           int head_dim, __bf16* __restrict__ out) {
+    constexpr int kGroups = kBM / kCombineQueries;   // workgroups per query tile
+    const int tile = blockIdx.x / kGroups;
+    const int h = tile / tiles_per_head;
+    const int vt = tile - h * tiles_per_head;
+    const int b = find_sequence(cu, num_seqs, vt);
+    const int seq_lo = cu[b], seq_hi = cu[b + 1];
+    const int q0 = seq_lo + (vt - (seq_lo / kBM + b)) * kBM;
+    const int qt = (blockIdx.x - tile * kGroups) * kCombineQueries + (int)(threadIdx.x >> 4);   // query in tile
+    const int c = threadIdx.x & 15;                                                             // 8-dim chunk
+    if (q0 + qt >= seq_hi || 8 * c >= head_dim) return;
+    const size_t split_rows = (size_t)num_heads * tiles_per_head * kBM;
+    const size_t row0 = ((size_t)h * tiles_per_head + vt) * kBM + qt;
+    // loops over kMaxSplits are unrolled, so the weights stay in registers
+    v2f ml[kMaxSplits];
+    float mmax = kMInit;
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplits; ++sp) {
+        ml[sp] = sp < num_splits ? part_ml[row0 + sp * split_rows] : v2f{kMInit, 0.0f};
+        if (ml[sp][1] > 0.0f) mmax = fmaxf(mmax, ml[sp][0]);
+    }
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float wsum = 0.0f;
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplits; ++sp) {
+        if (!(ml[sp][1] > 0.0f)) continue;
+        const float wt = __builtin_amdgcn_exp2f(ml[sp][0] - mmax) * ml[sp][1];
+        wsum += wt;
+        const f16x8 x = *(const f16x8*)(part_o + (row0 + sp * split_rows) * kD + 8 * c);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += wt * (float)x[i];
+    }
+    const float f = scales[2] / wsum;
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = (__bf16)(acc[i] * f);
+    *(bf16x8*)(out + ((size_t)(q0 + qt) * num_heads + h) * head_dim + 8 * c) = r;
+}
+
+// The smallest instantiation whose 32-dim chunks and 16-dim blocks cover head_dim.
+template <bool kPartial>
+auto* attention_kernel_for(int head_dim) {
+    auto* kernel = attn_fwd_kernel<4, 8, kPartial>;
+    if (head_dim <= 32) kernel = attn_fwd_kernel<1, 2, kPartial>;
+    else if (head_dim <= 64) kernel = attn_fwd_kernel<2, 4, kPartial>;
+    else if (head_dim <= 80) kernel = attn_fwd_kernel<3, 5, kPartial>;
+    else if (head_dim <= 96) kernel = attn_fwd_kernel<3, 6, kPartial>;
+    return kernel;
+}
+
+// log2(e) / sqrt(head_dim) in float32: for head_dim 128 this is the product
+// of the two float32 constants.
+float softmax_log2_factor(int head_dim) {
+    const float rsqrt_d = head_dim == kD ? kRsqrtD : (float)(1.0 / std::sqrt((double)head_dim));
+    return kLog2e * rsqrt_d;
+}
+
 }  // namespace
+
+size_t attention_workspace_bytes(int num_seqs, int total_tokens, int num_heads, int num_splits) {
+    if (num_splits <= 1) return 0;
+    const size_t rows = (size_t)num_splits * num_heads * tiles_per_head(total_tokens, num_seqs) * kBM;
+    const size_t o_bytes = (rows * kD * sizeof(_Float16) + 255) & ~(size_t)255;
+    return o_bytes + rows * 2 * sizeof(float);
+}
 
 hipError_t launch_attention(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* scales,
                             const int32_t* cu_seqlens, int num_seqs, int total_tokens, int num_heads, int head_dim,
                             void* out, hipStream_t s) {
+    return launch_attention_split(q8, k8, v8, scales, cu_seqlens, num_seqs, total_tokens, num_heads, head_dim, 1,
+                                  nullptr, out, s);
+}
+
+hipError_t launch_attention_split(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* scales,
+                                  const int32_t* cu_seqlens, int num_seqs, int total_tokens, int num_heads,
+                                  int head_dim, int num_splits, void* workspace, void* out, hipStream_t s) {
     const int tph = tiles_per_head(total_tokens, num_seqs);
     const long long nwg = (long long)tph * num_heads;
     if (nwg <= 0) return hipSuccess;
-    if (nwg > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-    // log2(e) / sqrt(head_dim) in float32: for head_dim 128 this is the
-    // product of the two float32 constants.
-    const float rsqrt_d = head_dim == kD ? kRsqrtD : (float)(1.0 / std::sqrt((double)head_dim));
-    const float c = kLog2e * rsqrt_d;
-    // the smallest instantiation whose 32-dim chunks and 16-dim blocks cover head_dim
-    auto* kernel = attn_fwd_kernel<4, 8>;
-    if (head_dim <= 32) kernel = attn_fwd_kernel<1, 2>;
-    else if (head_dim <= 64) kernel = attn_fwd_kernel<2, 4>;
-    else if (head_dim <= 80) kernel = attn_fwd_kernel<3, 5>;
-    else if (head_dim <= 96) kernel = attn_fwd_kernel<3, 6>;
-    kernel<<<(unsigned)nwg, kThreads, 0, s>>>(q8, k8, v8, scales, cu_seqlens, num_seqs, num_heads, tph, head_dim, c,
-                                              (__bf16*)out);
+    if (nwg * num_splits > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+    const float c = softmax_log2_factor(head_dim);
+    if (num_splits <= 1) {
+        attention_kernel_for<false>(head_dim)<<<(unsigned)nwg, kThreads, 0, s>>>(
+            q8, k8, v8, scales, cu_seqlens, num_seqs, num_heads, tph, 1, head_dim, c, (__bf16*)out, nullptr, nullptr);
+        return hipGetLastError();
+    }
+    const size_t rows = (size_t)num_splits * nwg * kBM;
+    _Float16* part_o = (_Float16*)workspace;
+    v2f* part_ml = (v2f*)((char*)workspace + ((rows * kD * sizeof(_Float16) + 255) & ~(size_t)255));
+    attention_kernel_for<true>(head_dim)<<<(unsigned)(nwg * num_splits), kThreads, 0, s>>>(
+        q8, k8, v8, scales, cu_seqlens, num_seqs, num_heads, tph, num_splits, head_dim, c, nullptr, part_o, part_ml);
+    attn_combine_kernel<<<(unsigned)(nwg * (kBM / kCombineQueries)), 256, 0, s>>>(
+        part_o, part_ml, scales, cu_seqlens, num_seqs, num_heads, tph, num_splits, head_dim, (__bf16*)out);
     return hipGetLastError();
 }
 

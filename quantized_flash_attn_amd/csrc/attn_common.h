@@ -40,10 +40,13 @@ constexpr float kRsqrtD = 0.08838834764831845f;  // 1/sqrt(128)
 // kernel) for P V.  mc may lag a tile's max by up to kRescaleSlack units, so
 // p <= 2^15.5 stays below fp16's largest value (65504 ~= 2^16); when a
 // tile's max exceeds it by more, mc moves kRescaleHeadroom units above that
-// max, so the next 11 units of growth need no rescale while the largest p of
-// the row stays >= 2^4.5, far from fp16's subnormal range (2^-14).
+// max, so the next 11.5 units of growth need no rescale while the largest p
+// of the row stays >= 2^4, far from fp16's subnormal range (2^-14).  The
+// headroom is a whole number so that the top weight right after a move is
+// exactly 2^4 (a one-key row then returns its value row exactly).
 constexpr float kRescaleSlack = 7.5f;
-constexpr float kRescaleHeadroom = 3.5f;
+constexpr float kRescaleHeadroom = 4.0f;
+constexpr int kMaxSplits = 16;                   // key ranges a split launch may use
 constexpr float kMInit = -1e30f;                 // finite "no max yet": every first tile rescales, to 0 * O
 
 // Buffer descriptor word 3 for raw byte addressing on gfx9-family GPUs.

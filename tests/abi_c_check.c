@@ -53,6 +53,14 @@ int main(void) {
            qfa_bf16_varlen_attn(dev, dev, dev, cu, 1, 4, 1, 64, dev, NULL), QFA_ERR_UNSUPPORTED);
     expect("export: null output", qfa_export_static_amax(&st, 1.5f, NULL, NULL), QFA_ERR_NULL);
     if (qfa_descale_ptr(&st) != NULL) { printf("FAIL descale pointer of an uninitialised state\n"); ++failures; }
+    expect("split: num_splits 17",
+           qfa_fp8_varlen_attn_split(dev, dev, dev, (const float*)dev, cu, 1, 300, 2, 128, 17, dev, (size_t)1 << 30,
+                                     dev, NULL), QFA_ERR_VALUE);
+    expect("split: no workspace",
+           qfa_fp8_varlen_attn_split(dev, dev, dev, (const float*)dev, cu, 1, 300, 2, 128, 4, NULL, 0, dev, NULL),
+           QFA_ERR_WORKSPACE);
+    if (qfa_fp8_varlen_attn_auto_splits(1, 8192, 16) != 1) { printf("FAIL auto splits of a full launch\n"); ++failures; }
+    if (qfa_fp8_varlen_attn_workspace_bytes(1, 2304, 8, 0) == 0) { printf("FAIL workspace bytes\n"); ++failures; }
 
     if (failures == 0) printf("C ABI checks ok\n");
     return failures == 0 ? 0 : 1;

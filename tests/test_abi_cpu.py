@@ -20,6 +20,7 @@ FAKE = 0x10000          # 16-byte aligned, never dereferenced
 MISALIGNED = 0x10004
 
 OK, NULL, SHAPE, UNSUP, ALIGN, MODE, NO_STATIC, VALUE, STATE = 0, 1, 2, 3, 4, 5, 6, 7, 8
+WORKSPACE = 11
 
 
 def header_functions():
@@ -30,7 +31,7 @@ def header_functions():
 
 def test_header_symbols_exported():
     declared = header_functions()
-    assert len(declared) == 12, declared
+    assert len(declared) == 15, declared
     out = subprocess.run(["nm", "-D", "--defined-only", qfa.library_path()], stdout=subprocess.PIPE, text=True).stdout
     exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
     missing = [f for f in declared if f not in exported]
@@ -40,8 +41,8 @@ def test_header_symbols_exported():
 
 def test_state_bytes_and_status_strings():
     assert 256 <= qfa.scale_state_bytes() <= 64 * 1024
-    for s in range(11):
-        assert lib.qfa_status_string(s)
+    for s in range(12):
+        assert lib.qfa_status_string(s) != b"unknown status", s
     assert lib.qfa_status_string(99) == b"unknown status"
 
 
@@ -120,6 +121,62 @@ def test_attention_validation():
         assert _attn(**{name: MISALIGNED}) == ALIGN
     assert _attn(sc=FAKE + 2) == ALIGN
     assert _attn(cu=FAKE + 1) == ALIGN
+
+
+def _split(q8=FAKE, k8=FAKE, v8=FAKE, sc=FAKE, cu=FAKE, B=1, T=300, H=2, D=128, S=0, ws=FAKE, wsb=1 << 30,
+           out=FAKE):
+    return lib.qfa_fp8_varlen_attn_split(q8, k8, v8, sc, cu, B, T, H, D, S, ws, wsb, out, None)
+
+
+def test_split_attention_validation():
+    # the checks shared with qfa_fp8_varlen_attn
+    assert _split(D=100) == UNSUP
+    assert _split(H=0) == SHAPE
+    assert _split(B=0) == SHAPE
+    assert _split(T=1, H=65537) == SHAPE
+    assert _split(sc=None) == NULL
+    for name in ("q8", "k8", "v8", "out"):
+        assert _split(**{name: None}) == NULL
+        assert _split(**{name: MISALIGNED}) == ALIGN
+    # split count and workspace
+    for bad in (-1, 17, 100):
+        assert _split(S=bad) == VALUE, bad
+    need = lib.qfa_fp8_varlen_attn_workspace_bytes(1, 300, 2, 4)
+    assert need > 0
+    assert _split(S=4, ws=None) == WORKSPACE
+    assert _split(S=4, wsb=need - 1) == WORKSPACE
+    assert _split(S=4, ws=MISALIGNED, wsb=need) == ALIGN
+    # the automatic count for 2304 tokens x 8 heads is above 1, so a workspace is required
+    assert lib.qfa_fp8_varlen_attn_auto_splits(1, 2304, 8) > 1
+    assert _split(S=0, ws=None, T=2304, H=8) == WORKSPACE
+    # ... and for 300 tokens x 2 heads it is 1: no workspace needed (validation passes; nothing to launch
+    # here would need a GPU, so only the count is checked)
+    assert lib.qfa_fp8_varlen_attn_auto_splits(1, 300, 2) == 1
+    assert b"workspace" in lib.qfa_last_error()
+
+
+def test_split_counts_and_workspace_sizes():
+    auto = lib.qfa_fp8_varlen_attn_auto_splits
+    wsb = lib.qfa_fp8_varlen_attn_workspace_bytes
+    # launches with a query tile per CU are not split
+    assert auto(1, 8192, 16) == 1 and wsb(1, 8192, 16, 0) == 0
+    assert auto(1, 8192, 8) == 1           # exactly 256 query tiles
+    assert auto(3, 43200, 16) == 1 and auto(4, 99504, 16) == 1
+    # as many ranges as fit one round of 256 workgroups, each of at least two key tiles
+    assert auto(1, 2304, 16) == 1          # 144 query tiles: two ranges would need a second round
+    assert auto(1, 2304, 8) == 3           # 72 query tiles x 3 ranges = 216
+    assert auto(1, 8192, 4) == 2           # 128 x 2 = 256
+    assert auto(1, 4096, 1) == 16          # 16 x 16, two key tiles per range
+    assert auto(1, 256, 2) == 1            # two key tiles: one range of two
+    assert auto(1, 1, 1) == 1
+    # bytes: S ranges x heads x virtual tiles (T/256 + B) x 256 rows x (128 fp16 + 2 float32)
+    for B, T, H, S in ((1, 2304, 16, 3), (4, 1000, 3, 5), (2, 257, 1, 16), (1, 2304, 8, 3)):
+        rows = S * H * (T // 256 + B) * 256
+        o = (rows * 256 + 255) // 256 * 256
+        assert wsb(B, T, H, S) == o + rows * 8, (B, T, H, S)
+    assert wsb(1, 2304, 16, 1) == 0 and wsb(1, 2304, 16, 0) == 0
+    assert wsb(1, 2304, 8, 0) == wsb(1, 2304, 8, 3)
+    assert wsb(1, 2304, 16, 17) == 0 and wsb(0, 2304, 16, 2) == 0 and wsb(1, -1, 16, 2) == 0
 
 
 def _packed(h, mode=0, qkv=FAKE, T=8, H=2, D=80, outs=(FAKE,) * 3):
