@@ -61,6 +61,7 @@ typedef enum qfa_mode {
 #define QFA_HEAD_DIM 128
 #define QFA_MAX_HISTORY 16
 #define QFA_MAX_SPLITS 16   /* key ranges per query tile in qfa_fp8_varlen_attn_split */
+#define QFA_NOALLOC_SCRATCH_BYTES ((size_t)36 << 20) /* workspace of qfa_fp8_varlen_attn_split_noalloc */
 
 /*
  * Host handle of one attention layer's scale state.  Filled by
@@ -212,6 +213,28 @@ qfa_status qfa_fp8_varlen_attn_split(const uint8_t* q8, const uint8_t* k8, const
                                      const float* scales, const int32_t* cu_seqlens, int num_seqs,
                                      int64_t total_tokens, int num_heads, int head_dim, int num_splits,
                                      void* workspace, size_t workspace_bytes, void* out, void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP-graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * qfa_fp8_varlen_attn_split with the library's own workspace instead of a
+ * caller-owned one.  That workspace is a fixed device array of
+ * QFA_NOALLOC_SCRATCH_BYTES (36 MiB) that each GPU the library runs on holds
+ * until the process ends; it covers every split count the automatic rule
+ * (num_splits = 0) picks.  A request needing more (an explicit num_splits on
+ * a large launch) returns QFA_ERR_WORKSPACE before anything is enqueued.
+ * The call enqueues kernels only: no hipMalloc, hipFree or other allocating
+ * routine; the array's address on the current device (which must be the
+ * stream's) is looked up once per device.  All calls on one GPU share that
+ * GPU's array, which keeps the last call's contents: calls that overlap on
+ * one GPU (other streams, other threads) race and must be ordered by the
+ * caller.  Nothing in the array needs to start at zero.  Other arguments and
+ * results as qfa_fp8_varlen_attn_split.
+ */
+qfa_status qfa_fp8_varlen_attn_split_noalloc(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                                             const float* scales, const int32_t* cu_seqlens, int num_seqs,
+                                             int64_t total_tokens, int num_heads, int head_dim, int num_splits,
+                                             void* out, void* stream);
 
 /*
  * Split count qfa_fp8_varlen_attn_split uses for num_splits = 0: as many

@@ -21,6 +21,8 @@ Entry points (same names as the C ABI without the ``qfa_`` prefix):
 * ``fp8_varlen_attn_split(q8, k8, v8, scales, cu_seqlens, num_heads, head_dim=128, num_splits=0,
   workspace=None, out=None)``: the same with each query tile's keys split into ranges (small images);
   ``workspace`` is a caller-owned uint8 device tensor (allocated here when not given)
+* ``fp8_varlen_attn_split_noalloc(q8, k8, v8, scales, cu_seqlens, num_heads, head_dim=128, num_splits=0,
+  out=None)``: the split launch on the library's own fixed workspace (the C entry allocates nothing)
 * ``fp8_varlen_attn_auto_splits(num_seqs, total_tokens, num_heads)``,
   ``fp8_varlen_attn_workspace_bytes(num_seqs, total_tokens, num_heads, num_splits=0)``
 * ``bf16_varlen_attn(q, k, v, cu_seqlens, num_heads, head_dim=128, out=None)`` (the BF16 baseline)
@@ -43,6 +45,7 @@ DYNAMIC = 0
 STATIC = 1
 HEAD_DIM = 128
 MAX_HISTORY = 16
+NOALLOC_SCRATCH_BYTES = 36 << 20   # QFA_NOALLOC_SCRATCH_BYTES
 
 _MODES = {"dynamic": DYNAMIC, "static": STATIC, DYNAMIC: DYNAMIC, STATIC: STATIC}
 
@@ -111,6 +114,7 @@ def _load():
         "qfa_fp8_varlen_attn": (i32, [vp, vp, vp, vp, vp, i32, i64, i32, i32, vp, vp]),
         "qfa_fp8_varlen_attn_split": (i32, [vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, vp, ctypes.c_size_t, vp,
                                             vp]),
+        "qfa_fp8_varlen_attn_split_noalloc": (i32, [vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, vp, vp]),
         "qfa_fp8_varlen_attn_auto_splits": (i32, [i32, i64, i32]),
         "qfa_fp8_varlen_attn_workspace_bytes": (ctypes.c_size_t, [i32, i64, i32, i32]),
         "qfa_bf16_varlen_attn": (i32, [vp, vp, vp, vp, i32, i64, i32, i32, vp, vp]),
@@ -138,6 +142,7 @@ EXPORTS = (
     "qfa_descale_ptr",
     "qfa_fp8_varlen_attn",
     "qfa_fp8_varlen_attn_split",
+    "qfa_fp8_varlen_attn_split_noalloc",
     "qfa_fp8_varlen_attn_auto_splits",
     "qfa_fp8_varlen_attn_workspace_bytes",
     "qfa_bf16_varlen_attn",
@@ -326,6 +331,18 @@ def fp8_varlen_attn_split(q8, k8, v8, scales, cu_seqlens, num_heads=None, head_d
                                               cu_seqlens.data_ptr(), B, T, H, head_dim, int(num_splits),
                                               workspace.data_ptr(), workspace.numel(), out.data_ptr(),
                                               _stream_ptr(q8.device)))
+    return out
+
+
+def fp8_varlen_attn_split_noalloc(q8, k8, v8, scales, cu_seqlens, num_heads=None, head_dim=HEAD_DIM, num_splits=0,
+                                  out=None):
+    """``fp8_varlen_attn_split`` on the library's own fixed workspace (36 MiB per GPU): the C entry point allocates
+    nothing.  Calls on one GPU share that workspace and must not overlap."""
+    T, H, out = _attn_args(q8, k8, v8, scales, cu_seqlens, num_heads, head_dim, out)
+    with torch.cuda.device(q8.device):
+        _check(_lib.qfa_fp8_varlen_attn_split_noalloc(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), scales.data_ptr(),
+                                                      cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, T, H, head_dim,
+                                                      int(num_splits), out.data_ptr(), _stream_ptr(q8.device)))
     return out
 
 

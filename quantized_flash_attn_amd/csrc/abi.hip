@@ -65,6 +65,8 @@ bool padded_head_dim_ok(int head_dim) { return head_dim >= 8 && head_dim <= QFA_
 
 extern "C" {
 
+static_assert(qfa::kAttnScratchBytes == QFA_NOALLOC_SCRATCH_BYTES, "scratch size and its public constant");
+
 size_t qfa_scale_state_bytes(void) { return sizeof(qfa::DeviceState); }
 
 const char* qfa_status_string(qfa_status s) {
@@ -261,6 +263,35 @@ qfa_status qfa_fp8_varlen_attn_split(const uint8_t* q8, const uint8_t* k8, const
     if (n == 0) return ok();
     const hipError_t e = qfa::launch_attention_split(q8, k8, v8, scales, cu_seqlens, num_seqs, (int)total_tokens,
                                                      num_heads, head_dim, sp, workspace, out, (hipStream_t)stream);
+    return check_launch(e, where);
+}
+
+qfa_status qfa_fp8_varlen_attn_split_noalloc(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                                             const float* scales, const int32_t* cu_seqlens, int num_seqs,
+                                             int64_t total_tokens, int num_heads, int head_dim, int num_splits,
+                                             void* out, void* stream) {
+    const char* where = "qfa_fp8_varlen_attn_split_noalloc";
+    int64_t n = 0;
+    qfa_status s = check_fp8_attn(q8, k8, v8, scales, cu_seqlens, num_seqs, total_tokens, num_heads, head_dim, out,
+                                  &n, where);
+    if (s != QFA_OK) return s;
+    if (num_splits < 0 || num_splits > QFA_MAX_SPLITS)
+        return fail(QFA_ERR_VALUE, "%s: num_splits %d not in 0..%d", where, num_splits, QFA_MAX_SPLITS);
+    const int sp = num_splits == 0 ? auto_splits(num_seqs, total_tokens, num_heads) : num_splits;
+    const size_t need = qfa::attention_workspace_bytes(num_seqs, (int)total_tokens, num_heads, sp);
+    if (need > QFA_NOALLOC_SCRATCH_BYTES)
+        return fail(QFA_ERR_WORKSPACE, "%s: %d key ranges need %zu bytes of workspace, above the library's %zu",
+                    where, sp, need, (size_t)QFA_NOALLOC_SCRATCH_BYTES);
+    s = check_pending(where);
+    if (s != QFA_OK) return s;
+    if (n == 0) return ok();
+    void* ws = nullptr;
+    if (sp > 1) {
+        const hipError_t e = qfa::attention_scratch(&ws);
+        if (e != hipSuccess) return check_launch(e, where);
+    }
+    const hipError_t e = qfa::launch_attention_split(q8, k8, v8, scales, cu_seqlens, num_seqs, (int)total_tokens,
+                                                     num_heads, head_dim, sp, ws, out, (hipStream_t)stream);
     return check_launch(e, where);
 }
 

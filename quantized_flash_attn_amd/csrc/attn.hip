@@ -70,6 +70,7 @@
 //   epilogue        out = bf16(O * s_v / l).
 
 #include <cmath>
+#include <mutex>
 
 #include "attn_common.h"
 
@@ -602,7 +603,35 @@ float softmax_log2_factor(int head_dim) {
     return kLog2e * rsqrt_d;
 }
 
+// Workspace of qfa_fp8_varlen_attn_split_noalloc, for callers that cannot
+// allocate device memory.  Each GPU the library runs on holds its own copy
+// until the process ends; its size covers every split count the automatic
+// rule picks (at most 512 virtual query tiles x 256 rows of 264 bytes, about
+// 33 MiB).  Host code never passes the array's name to a kernel (on the host
+// it is a stand-in, not a device address): it passes the address
+// hipGetSymbolAddress returns for the current device.
+__device__ __attribute__((aligned(256))) unsigned char scratch[kAttnScratchBytes];
+
 }  // namespace
+
+hipError_t attention_scratch(void** ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 size_t attention_workspace_bytes(int num_seqs, int total_tokens, int num_heads, int num_splits) {
     if (num_splits <= 1) return 0;

@@ -47,6 +47,11 @@ hipError_t launch_attention(const uint8_t* q8, const uint8_t* k8, const uint8_t*
 // results in `workspace` (attention_workspace_bytes), merged by a second
 // kernel; num_splits <= 1 is launch_attention.
 size_t attention_workspace_bytes(int num_seqs, int total_tokens, int num_heads, int num_splits);
+// The library's own split workspace on the current device (a file-scope
+// device array of kAttnScratchBytes; its address is looked up once per
+// device).  No allocation.
+constexpr size_t kAttnScratchBytes = (size_t)36 << 20;
+hipError_t attention_scratch(void** ptr);
 hipError_t launch_attention_split(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* scales,
                                   const int32_t* cu_seqlens, int num_seqs, int total_tokens, int num_heads,
                                   int head_dim, int num_splits, void* workspace, void* out, hipStream_t s);

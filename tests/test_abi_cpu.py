@@ -31,7 +31,7 @@ def header_functions():
 
 def test_header_symbols_exported():
     declared = header_functions()
-    assert len(declared) == 15, declared
+    assert len(declared) == 16, declared
     out = subprocess.run(["nm", "-D", "--defined-only", qfa.library_path()], stdout=subprocess.PIPE, text=True).stdout
     exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
     missing = [f for f in declared if f not in exported]
@@ -153,6 +153,23 @@ def test_split_attention_validation():
     # here would need a GPU, so only the count is checked)
     assert lib.qfa_fp8_varlen_attn_auto_splits(1, 300, 2) == 1
     assert b"workspace" in lib.qfa_last_error()
+
+
+def test_noalloc_split_validation():
+    def na(B=1, T=2304, H=8, D=128, S=0, out=FAKE, sc=FAKE):
+        return lib.qfa_fp8_varlen_attn_split_noalloc(FAKE, FAKE, FAKE, sc, FAKE, B, T, H, D, S, out, None)
+    assert na(D=100) == UNSUP
+    assert na(sc=None) == NULL
+    assert na(out=MISALIGNED) == ALIGN
+    assert na(S=17) == VALUE and na(S=-1) == VALUE
+    # requests beyond the library's fixed workspace are refused before anything is enqueued
+    assert lib.qfa_fp8_varlen_attn_workspace_bytes(1, 99504, 16, 16) > qfa.NOALLOC_SCRATCH_BYTES
+    assert na(T=99504, H=16, S=16) == WORKSPACE
+    assert b"workspace" in lib.qfa_last_error()
+    # every automatic split count fits it (at most 512 virtual query tiles x 256 rows of 264 bytes)
+    assert 512 * 256 * 264 <= qfa.NOALLOC_SCRATCH_BYTES
+    for B, T, H in ((1, 2304, 8), (1, 8192, 4), (1, 4096, 1), (1, 2304, 1), (3, 700, 5), (1, 60000, 2)):
+        assert lib.qfa_fp8_varlen_attn_workspace_bytes(B, T, H, 0) <= qfa.NOALLOC_SCRATCH_BYTES, (B, T, H)
 
 
 def test_split_counts_and_workspace_sizes():
