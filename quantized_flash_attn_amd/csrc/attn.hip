@@ -263,6 +263,7 @@ __device__ __forceinline__ void row_sums(const f16x8 (&pop)[kQB][4], v4f (&l)[kQ
 template <int kDB_>
 struct Wave {
     static constexpr int kDB = kDB_;
+    static constexpr bool kBlockRescale = true;   // rescale decisions per 16-query block
     const uint8_t* k8;
     const uint8_t* v8;
     uint32_t row_stride;   // bytes between tokens of one head (uniform)

@@ -61,6 +61,7 @@ __device__ inline void issue_tile_load(const unsigned char* __restrict__ src, ui
 // columns = queries; output: rows = head dims, columns = queries).
 struct Wave {
     static constexpr int kDB = 8;   // live 16-dim output blocks
+    static constexpr bool kBlockRescale = false;   // one rescale decision per wave (fewer registers)
     const unsigned char* k;
     const unsigned char* v;
     uint32_t row_stride;   // bytes between tokens of one head (uniform)

@@ -133,10 +133,11 @@ __device__ __forceinline__ void exp_blocks(const W& w, v4f (&s)[8][kQB], int nk)
 
 // Online-softmax step for one key tile with nk valid keys, first part:
 // mask the keys past nk and take each query's tile max tm (log2 units).  For
-// each 16-query block separately: if tm exceeds the running max mc by more
-// than the slack for any of its queries, move mc to max(mc, tm + headroom)
-// for each of them and rescale that block's O and l (which hold the earlier
-// tiles) by 2^(mc_old - mc_new).  Then turn the scores of key blocks
+// each 16-query block separately (W::kBlockRescale; else for the wave's 32
+// queries together): if tm exceeds the running max mc by more than the slack
+// for any of its queries, move mc to max(mc, tm + headroom) for each of them
+// and rescale that block's O and l (which hold the earlier tiles) by
+// 2^(mc_old - mc_new).  Then turn the scores of key blocks
 // [0, kSplit) into p = 2^(S c + 8 - mc); the rest follow with
 // exp_blocks<kSplit, 8>.  s[kb][qb] holds keys 16kb + 4g + i of query r16
 // (lane (r16, g), g4 = 4g).  W carries mc[kQB], l[kQB], o[8][kQB] (of which
@@ -153,6 +154,7 @@ __device__ __forceinline__ void softmax_head(W& w, v4f (&s)[8][kQB], int nk) {
                 for (int qb = 0; qb < kQB; ++qb) s[kb][qb][i] = dead ? -INFINITY : s[kb][qb][i];
             }
     }
+    float tm[kQB];
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
         float mx = s[0][qb][0];
@@ -160,15 +162,27 @@ __device__ __forceinline__ void softmax_head(W& w, v4f (&s)[8][kQB], int nk) {
         for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][qb][i]);
-        const float tm = quad_max(mx) * w.cexp;
-        if (__any(tm - w.mc[qb] > kRescaleSlack)) {
-            const float mc = fmaxf(w.mc[qb], tm + kRescaleHeadroom);
-            const float alpha = __builtin_amdgcn_exp2f(w.mc[qb] - mc);
-            w.mc[qb] = mc;
-            w.l[qb] *= alpha;
+        tm[qb] = quad_max(mx) * w.cexp;
+    }
+    auto rescale = [&](int qb) {
+        const float mc = fmaxf(w.mc[qb], tm[qb] + kRescaleHeadroom);
+        const float alpha = __builtin_amdgcn_exp2f(w.mc[qb] - mc);
+        w.mc[qb] = mc;
+        w.l[qb] *= alpha;
 #pragma unroll
-            for (int db = 0; db < W::kDB; ++db) w.o[db][qb] *= alpha;
-        }
+        for (int db = 0; db < W::kDB; ++db) w.o[db][qb] *= alpha;
+    };
+    if constexpr (W::kBlockRescale) {   // one decision per 16-query block
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb)
+            if (__any(tm[qb] - w.mc[qb] > kRescaleSlack)) rescale(qb);
+    } else {                            // one decision for the wave's 32 queries
+        bool grow = false;
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) grow |= tm[qb] - w.mc[qb] > kRescaleSlack;
+        if (__any(grow))
+#pragma unroll
+            for (int qb = 0; qb < kQB; ++qb) rescale(qb);
     }
     exp_blocks<0, kSplit>(w, s, nk);
 }
