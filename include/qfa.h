@@ -177,8 +177,9 @@ const float* qfa_descale_ptr(const qfa_scale_state* st);
  *                  cu[num_seqs] = total_tokens; empty sequences are allowed
  *   head_dim       8..128 in steps of 8 (128 for qfa_quantize_qkv's codes)
  *   out            device bf16 [total_tokens, num_heads, head_dim] (out)
- * total_tokens must be below 2^31 and num_heads at most 65536
- * (QFA_ERR_SHAPE otherwise).  The kernel converts the codes exactly to
+ * total_tokens must be below 2^31, num_seqs at most 2^30 and num_heads at
+ * most 65536, and (total_tokens / 256 + num_seqs) * num_heads workgroups
+ * must fit an int (QFA_ERR_SHAPE otherwise).  The kernel converts the codes exactly to
  * fp16 and runs both products on fp16 MFMAs with float32 accumulation; the
  * probabilities are rounded to fp16 for the P*V product.
  */
@@ -206,8 +207,9 @@ qfa_status qfa_fp8_varlen_attn(const uint8_t* q8, const uint8_t* k8, const uint8
  *                    NULL when the split count resolves to 1.  Its contents
  *                    on entry do not matter and are garbage on return.
  *   workspace_bytes  its size (QFA_ERR_WORKSPACE if too small or missing)
- * QFA_ERR_VALUE for num_splits outside 0..16.  Calls sharing one workspace
- * must be ordered on one stream.
+ * QFA_ERR_VALUE for num_splits outside 0..16; QFA_ERR_SHAPE when the
+ * workgroups times the ranges, or 16 merge workgroups per query tile, exceed
+ * an int.  Calls sharing one workspace must be ordered on one stream.
  */
 qfa_status qfa_fp8_varlen_attn_split(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                                      const float* scales, const int32_t* cu_seqlens, int num_seqs,
@@ -242,7 +244,8 @@ qfa_status qfa_fp8_varlen_attn_split_noalloc(const uint8_t* q8, const uint8_t* k
  * compute units (256-query tiles x heads x ranges <= 256), each of at least
  * two 128-key tiles of a sequence of the batch's mean length, at most 16; 1
  * when that is fewer than two.  (A second round of workgroups costs about
- * what the split saves.)  Host-only, no device access.
+ * what the split saves.)  Host-only, no device access; 1 for sizes the attention
+ * entry points refuse.
  */
 int qfa_fp8_varlen_attn_auto_splits(int num_seqs, int64_t total_tokens, int num_heads);
 
@@ -263,7 +266,7 @@ size_t qfa_fp8_varlen_attn_workspace_bytes(int num_seqs, int64_t total_tokens, i
  *   q, k, v        device bf16 [total_tokens, num_heads, 128]
  *   cu_seqlens     device int32[num_seqs + 1], same rules as qfa_fp8_varlen_attn
  *   out            device bf16 [total_tokens, num_heads, 128] (out)
- * total_tokens must be below 2^31 and num_heads at most 65536.  Products
+ * Size limits as qfa_fp8_varlen_attn.  Products
  * and sums run in fp32 on bf16
  * MFMA operands; the probabilities are rounded to bf16 for the P*V product.
  * Same status codes as qfa_fp8_varlen_attn.

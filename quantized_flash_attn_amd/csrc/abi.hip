@@ -58,6 +58,22 @@ qfa_status check_shape(int64_t total_tokens, int num_heads, int head_dim, int64_
 // num_heads * 256 bytes (bf16); 65536 heads keep it below 2^31.
 constexpr int kMaxAttnHeads = 65536;
 
+// Sequences per launch: at most 2^30, so that the virtual query tiles of one
+// head (total_tokens / 256 + num_seqs, total_tokens < 2^31) fit an int.
+constexpr int kMaxSeqs = 1 << 30;
+
+// The attention grids: (total_tokens / 256 + num_seqs) query tiles per head
+// times num_heads workgroups, times the key ranges of a split launch, whose
+// merge adds 16 workgroups per query tile; each must fit an int.
+qfa_status check_attn_grid(int num_seqs, int64_t total_tokens, int num_heads, int splits, const char* where) {
+    const int64_t tiles = (total_tokens / 256 + num_seqs) * (int64_t)num_heads;
+    const int64_t limit = INT64_C(0x7FFFFFFF);
+    if (tiles * std::max(splits, 1) > limit || (splits > 1 && tiles * 16 > limit))
+        return fail(QFA_ERR_SHAPE, "%s: %lld query tiles x %d key ranges exceed the grid limit", where,
+                    (long long)tiles, splits);
+    return QFA_OK;
+}
+
 // Head dims the padded paths accept: 8..128 in steps of 8 (16-byte bf16 rows).
 bool padded_head_dim_ok(int head_dim) { return head_dim >= 8 && head_dim <= QFA_HEAD_DIM && head_dim % 8 == 0; }
 
@@ -70,7 +86,12 @@ static_assert(qfa::kAttnScratchBytes == QFA_NOALLOC_SCRATCH_BYTES, "scratch size
 size_t qfa_scale_state_bytes(void) { return sizeof(qfa::DeviceState); }
 
 const char* qfa_status_string(qfa_status s) {
-    switch (s) {
+    // A C caller may pass any int; reading it as the C++ enum would be
+    // undefined outside the declared codes, so take its bits as an int.
+    static_assert(sizeof(qfa_status) == sizeof(int), "qfa_status is an int-sized enum");
+    int code;
+    memcpy(&code, &s, sizeof code);
+    switch (code) {
         case QFA_OK: return "ok";
         case QFA_ERR_NULL: return "null pointer";
         case QFA_ERR_SHAPE: return "invalid shape";
@@ -193,7 +214,8 @@ qfa_status check_fp8_attn(const uint8_t* q8, const uint8_t* k8, const uint8_t* v
         return fail(QFA_ERR_UNSUPPORTED, "%s: head_dim %d (8..128 in steps of 8)", where, head_dim);
     qfa_status s = check_shape(total_tokens, num_heads, QFA_HEAD_DIM, n, where);  // code rows are 128 wide
     if (s != QFA_OK) return s;
-    if (num_seqs < 1) return fail(QFA_ERR_SHAPE, "%s: num_seqs %d must be at least 1", where, num_seqs);
+    if (num_seqs < 1 || num_seqs > kMaxSeqs)
+        return fail(QFA_ERR_SHAPE, "%s: num_seqs %d not in 1..2^30", where, num_seqs);
     if (total_tokens >= (INT64_C(1) << 31)) return fail(QFA_ERR_SHAPE, "%s: total_tokens must be below 2^31", where);
     if (num_heads > kMaxAttnHeads)
         return fail(QFA_ERR_SHAPE, "%s: num_heads %d above %d", where, num_heads, kMaxAttnHeads);
@@ -215,7 +237,10 @@ qfa_status check_fp8_attn(const uint8_t* q8, const uint8_t* k8, const uint8_t* v
 // split only matters for small batches, whose images are of similar size),
 // at most QFA_MAX_SPLITS; 1 when that is fewer than two ranges.
 int auto_splits(int num_seqs, int64_t total_tokens, int num_heads) {
-    if (total_tokens <= 0 || num_seqs < 1 || num_heads < 1) return 1;
+    // sizes the attention entry points refuse get 1 (and no overflow below)
+    if (total_tokens <= 0 || total_tokens >= (INT64_C(1) << 31) || num_seqs < 1 || num_seqs > kMaxSeqs ||
+        num_heads < 1)
+        return 1;
     const int64_t query_tiles = ((total_tokens + 255) / 256 + (num_seqs - 1)) * num_heads;
     const int64_t mean_len = (total_tokens + num_seqs - 1) / num_seqs;
     const int64_t nt = (mean_len + 127) / 128;
@@ -233,7 +258,9 @@ int qfa_fp8_varlen_attn_auto_splits(int num_seqs, int64_t total_tokens, int num_
 }
 
 size_t qfa_fp8_varlen_attn_workspace_bytes(int num_seqs, int64_t total_tokens, int num_heads, int num_splits) {
-    if (num_seqs < 1 || num_heads < 1 || total_tokens < 0 || total_tokens >= (INT64_C(1) << 31)) return 0;
+    if (num_seqs < 1 || num_seqs > kMaxSeqs || num_heads < 1 || num_heads > kMaxAttnHeads || total_tokens < 0 ||
+        total_tokens >= (INT64_C(1) << 31))
+        return 0;
     if (num_splits < 0 || num_splits > QFA_MAX_SPLITS) return 0;
     const int sp = num_splits == 0 ? auto_splits(num_seqs, total_tokens, num_heads) : num_splits;
     return qfa::attention_workspace_bytes(num_seqs, (int)total_tokens, num_heads, sp);
@@ -251,6 +278,8 @@ qfa_status qfa_fp8_varlen_attn_split(const uint8_t* q8, const uint8_t* k8, const
     if (num_splits < 0 || num_splits > QFA_MAX_SPLITS)
         return fail(QFA_ERR_VALUE, "%s: num_splits %d not in 0..%d", where, num_splits, QFA_MAX_SPLITS);
     const int sp = num_splits == 0 ? auto_splits(num_seqs, total_tokens, num_heads) : num_splits;
+    s = check_attn_grid(num_seqs, total_tokens, num_heads, sp, where);
+    if (s != QFA_OK) return s;
     const size_t need = qfa::attention_workspace_bytes(num_seqs, (int)total_tokens, num_heads, sp);
     if (n > 0 && sp > 1) {
         if (!workspace) return fail(QFA_ERR_WORKSPACE, "%s: %d key ranges need a workspace", where, sp);
@@ -278,6 +307,8 @@ qfa_status qfa_fp8_varlen_attn_split_noalloc(const uint8_t* q8, const uint8_t* k
     if (num_splits < 0 || num_splits > QFA_MAX_SPLITS)
         return fail(QFA_ERR_VALUE, "%s: num_splits %d not in 0..%d", where, num_splits, QFA_MAX_SPLITS);
     const int sp = num_splits == 0 ? auto_splits(num_seqs, total_tokens, num_heads) : num_splits;
+    s = check_attn_grid(num_seqs, total_tokens, num_heads, sp, where);
+    if (s != QFA_OK) return s;
     const size_t need = qfa::attention_workspace_bytes(num_seqs, (int)total_tokens, num_heads, sp);
     if (need > QFA_NOALLOC_SCRATCH_BYTES)
         return fail(QFA_ERR_WORKSPACE, "%s: %d key ranges need %zu bytes of workspace, above the library's %zu",
@@ -303,6 +334,8 @@ qfa_status qfa_fp8_varlen_attn(const uint8_t* q8, const uint8_t* k8, const uint8
     qfa_status s = check_fp8_attn(q8, k8, v8, scales, cu_seqlens, num_seqs, total_tokens, num_heads, head_dim, out,
                                   &n, where);
     if (s != QFA_OK) return s;
+    s = check_attn_grid(num_seqs, total_tokens, num_heads, 1, where);
+    if (s != QFA_OK) return s;
     s = check_pending(where);
     if (s != QFA_OK) return s;
     if (n == 0) return ok();
@@ -317,10 +350,13 @@ qfa_status qfa_bf16_varlen_attn(const void* q, const void* k, const void* v, con
     int64_t n = 0;
     qfa_status s = check_shape(total_tokens, num_heads, head_dim, &n, where);
     if (s != QFA_OK) return s;
-    if (num_seqs < 1) return fail(QFA_ERR_SHAPE, "%s: num_seqs %d must be at least 1", where, num_seqs);
+    if (num_seqs < 1 || num_seqs > kMaxSeqs)
+        return fail(QFA_ERR_SHAPE, "%s: num_seqs %d not in 1..2^30", where, num_seqs);
     if (total_tokens >= (INT64_C(1) << 31)) return fail(QFA_ERR_SHAPE, "%s: total_tokens must be below 2^31", where);
     if (num_heads > kMaxAttnHeads)
         return fail(QFA_ERR_SHAPE, "%s: num_heads %d above %d", where, num_heads, kMaxAttnHeads);
+    s = check_attn_grid(num_seqs, total_tokens, num_heads, 1, where);
+    if (s != QFA_OK) return s;
     if (!cu_seqlens) return fail(QFA_ERR_NULL, "%s: null cu_seqlens", where);
     if (n > 0 && (!q || !k || !v || !out)) return fail(QFA_ERR_NULL, "%s: null tensor pointer", where);
     if (n > 0 && !(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out)))
@@ -381,7 +417,8 @@ qfa_status qfa_export_static_amax(const qfa_scale_state* st, float margin, float
 qfa_status qfa_check_cu_seqlens(const int32_t* cu_seqlens, int num_seqs, int64_t total_tokens, void* stream) {
     const char* where = "qfa_check_cu_seqlens";
     if (!cu_seqlens) return fail(QFA_ERR_NULL, "%s: null cu_seqlens", where);
-    if (num_seqs < 1) return fail(QFA_ERR_SHAPE, "%s: num_seqs %d must be at least 1", where, num_seqs);
+    if (num_seqs < 1 || num_seqs > kMaxSeqs)
+        return fail(QFA_ERR_SHAPE, "%s: num_seqs %d not in 1..2^30", where, num_seqs);
     if (total_tokens < 0 || total_tokens >= (INT64_C(1) << 31)) return fail(QFA_ERR_SHAPE, "%s: total_tokens out of range", where);
     int32_t* h = (int32_t*)malloc(sizeof(int32_t) * ((size_t)num_seqs + 1));
     if (!h) return fail(QFA_ERR_SHAPE, "%s: host allocation failed", where);

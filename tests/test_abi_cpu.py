@@ -121,6 +121,11 @@ def test_attention_validation():
         assert _attn(**{name: MISALIGNED}) == ALIGN
     assert _attn(sc=FAKE + 2) == ALIGN
     assert _attn(cu=FAKE + 1) == ALIGN
+    # sequence count and grid: (T/256 + B) query tiles per head, times the heads, must fit an int
+    assert _attn(B=(1 << 30) + 1) == SHAPE
+    assert _attn(B=2 ** 31 - 1, T=(1 << 31) - 1) == SHAPE
+    assert _attn(B=1 << 30, T=8, H=4) == SHAPE
+    assert b"grid" in lib.qfa_last_error()
 
 
 def _split(q8=FAKE, k8=FAKE, v8=FAKE, sc=FAKE, cu=FAKE, B=1, T=300, H=2, D=128, S=0, ws=FAKE, wsb=1 << 30,
@@ -153,6 +158,10 @@ def test_split_attention_validation():
     # here would need a GPU, so only the count is checked)
     assert lib.qfa_fp8_varlen_attn_auto_splits(1, 300, 2) == 1
     assert b"workspace" in lib.qfa_last_error()
+    # 16 ranges, or 16 merge workgroups per query tile, past the grid limit
+    assert _split(B=1 << 26, T=8, H=2, S=16, wsb=2 ** 62) == SHAPE
+    assert _split(B=1 << 26, T=8, H=2, S=2, wsb=2 ** 62) == SHAPE
+    assert b"grid" in lib.qfa_last_error()
 
 
 def test_noalloc_split_validation():
@@ -194,6 +203,9 @@ def test_split_counts_and_workspace_sizes():
     assert wsb(1, 2304, 16, 1) == 0 and wsb(1, 2304, 16, 0) == 0
     assert wsb(1, 2304, 8, 0) == wsb(1, 2304, 8, 3)
     assert wsb(1, 2304, 16, 17) == 0 and wsb(0, 2304, 16, 2) == 0 and wsb(1, -1, 16, 2) == 0
+    # out-of-range sizes: no count above 1, no workspace, no overflow
+    assert auto(1, 2 ** 63 - 1, 16) == 1 and auto(2 ** 31 - 1, 1000, 1) == 1 and auto(1, 1 << 31, 1) == 1
+    assert wsb(1, 1 << 31, 1, 2) == 0 and wsb((1 << 30) + 1, 8, 1, 2) == 0 and wsb(1, 2304, 65537, 2) == 0
 
 
 def _packed(h, mode=0, qkv=FAKE, T=8, H=2, D=80, outs=(FAKE,) * 3):

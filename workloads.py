@@ -132,19 +132,20 @@ def random_qkv(seqlens, num_heads, seed, device="cpu", sigma=1.0, outlier_p=0.0,
     return tuple(_draw(shape, sig, outlier_p, outlier_scale, seed + t, device) for t in range(3))
 
 
-def ramp_qkv(seqlens, num_heads, seed, device="cpu", order="increasing") -> tuple:
+def ramp_qkv(seqlens, num_heads, seed, device="cpu", order="increasing", gain=4.0) -> tuple:
     """Seeded bf16 Q, K, V whose logits move steadily along each sequence.
 
     Every query of a head is a small perturbation of one positive direction
     u_h (entries in [1, 2)), and key j of a sequence of n tokens is
-    4 u_h * s_j with s_j rising from 0.05 to 1 over the sequence (``order``
-    "increasing") or falling from 1 to 0.05 ("decreasing").  The scaled
-    logits then grow by about 18 log2 units per 128 keys of a 1000-token
-    sequence (faster in shorter ones) for the increasing order, more than a
-    running max may lag plus the margin it keeps after moving, so the running
-    row max moves at every key tile (except a ragged last tile of one key);
-    for the decreasing order it never moves after the first tile.  V is
-    N(0, 1).
+    gain * u_h * s_j with s_j rising from 0.05 to 1 over the sequence
+    (``order`` "increasing") or falling from 1 to 0.05 ("decreasing").  With
+    the default gain of 4 the scaled logits grow by about 18 log2 units per
+    128 keys of a 1000-token sequence (faster in shorter ones) for the
+    increasing order, more than a running max may lag plus the margin it
+    keeps after moving, so the running row max moves at every key tile
+    (except a ragged last tile of one key); for the decreasing order it never
+    moves after the first tile.  The growth is proportional to the gain:
+    gains near 1.8 put it near 8 log2 units per tile.  V is N(0, 1).
     """
     T = int(sum(seqlens))
     g = torch.Generator(device="cpu")
@@ -156,6 +157,6 @@ def ramp_qkv(seqlens, num_heads, seed, device="cpu", order="increasing") -> tupl
         r = torch.linspace(0.05, 1.0, int(n)) if int(n) > 1 else torch.ones(int(n))
         s.append(r if order == "increasing" else r.flip(0))
     s = torch.cat(s) if s else torch.zeros(0)
-    k = 4.0 * u.expand(T, num_heads, HEAD_DIM) * s.view(-1, 1, 1)
+    k = gain * u.expand(T, num_heads, HEAD_DIM) * s.view(-1, 1, 1)
     v = torch.randn((T, num_heads, HEAD_DIM), generator=g)
     return tuple(t.to(torch.bfloat16).to(device) for t in (q, k, v))
