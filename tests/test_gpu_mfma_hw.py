@@ -10,14 +10,18 @@ c + sum_k a_k b_k over one group of 8 consecutive products:
 * the fp8 MFMAs (v_mfma_f32_16x16x128_f8f6f4 and v_mfma_f32_16x16x32_fp8_fp8)
   add a group of 8 products on a window of about 13 bits below the group's
   largest product and truncate the rest: 2^14 + 7 * 1 comes out as 2^14, and
-  2^11 + 7 * 0.875 as 2^11 + 7 * 0.75.  The accumulator input is added to the
-  group's sum exactly (65536 + 7 stays 65543);
+  2^11 + 7 * 0.875 as 2^11 + 7 * 0.75.  Each product is cut to a multiple of
+  2^(E - 13), E the exponent of the group's largest product, toward zero
+  (2^11 - 7 * 0.875 gives 2^11 - 7 * 0.75).  The accumulator input is added
+  to the group's sum exactly (65536 + 7 stays 65543);
 * the fp16 and bf16 MFMAs return the exact sums (every product of two E4M3
   values has at most 8 significant bits, and these sums fit fp32).
 
 With x20 outliers in both Q and K, a query and key sharing an outlier
 dimension have a product near 2^13-2^17 in one group, so the fp8 MFMAs would
-truncate the other 7 products of that group and move dominant logits.
+truncate the other 7 products of that group and move dominant logits
+(tests/test_fp8_mfma_emulation.py works out what that does to the
+workloads' attention on the CPU).
 """
 
 import ctypes
@@ -82,12 +86,13 @@ CASES = [
     ("2^14 + 7 x 1", [128.0] + [1.0] * 7, [128.0] + [1.0] * 7, 0.0, 16391.0),
     ("2^11 + 7 x 0.875", [64.0] + [0.875] * 7, [32.0] + [1.0] * 7, 0.0, 2054.125),
     ("65536 acc + 7", [7.0], [1.0], 65536.0, 65543.0),
+    ("2^11 - 7 x 0.875", [64.0] + [-0.875] * 7, [32.0] + [1.0] * 7, 0.0, 2041.875),
 ]
 
 # What gfx950 returns for the fp8 instructions: truncated group sums, exact accumulator add.
 FP8_OBSERVED = {
-    "f8f6f4_k128": [16384.0, 2053.25, 65543.0],
-    "fp8_k32": [16384.0, 2053.25, 65543.0],
+    "f8f6f4_k128": [16384.0, 2053.25, 65543.0, 2042.75],
+    "fp8_k32": [16384.0, 2053.25, 65543.0, 2042.75],
 }
 
 
