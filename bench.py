@@ -570,7 +570,9 @@ def main():
         "design_mfma_ceiling": {
             "frac_fp8_peak": 0.5,
             "why": "both products run on the fp16 MFMA (exact for E4M3 codes; half the fp8 rate) because gfx950's "
-                   "fp8 MFMAs truncate inside each group of 8 products (tests/test_gpu_mfma_hw.py)"},
+                   "fp8 MFMAs truncate inside each group of 8 products (tests/test_gpu_mfma_hw.py), which on this "
+                   "workload's outliers breaks the accuracy bound (tests/test_fp8_mfma_emulation.py)",
+            "frac_of_ceiling": round(attn_tflops / FP8_PEAK_TFLOPS / 0.5, 4)},
         "wall_s_timed_region": round(wall, 4),
     }
     if w.index == 3 and not args.no_as_specified:
