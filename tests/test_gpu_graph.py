@@ -96,3 +96,48 @@ def test_graph_replays_match_eager(name, w, seqlens, H, mode):
         # the replay's codes are the oracle's codes for this forward's inputs
         assert np.array_equal(codes(q8), oracle.quantize(bf16_to_f32(wq[0]), ost.inv[0])), r
     log(f"  5 replays bit-identical to eager; cursor {gs['cursor']}")
+
+
+def test_graph_split_noalloc_replays_match_eager():
+    """Quantize + the no-allocation split-key attention captured in one graph: the capture allocates nothing
+    (the split workspace is the library's fixed device array), and every replay equals the eager forward bit for
+    bit.  2304 tokens x 8 heads, dynamic: the automatic rule splits the keys into 3 ranges."""
+    seqlens, H, mode = (2304,), 8, "dynamic"
+    T = sum(seqlens)
+    assert qfa.fp8_varlen_attn_auto_splits(1, T, H) == 3
+    log(f"graph case: split no-allocation attention, T {T}, H {H}, {mode}")
+    w = WORKLOADS[3]
+    qs, ks, vs = (torch.zeros((T, H, HEAD_DIM), dtype=torch.bfloat16, device=DEV) for _ in range(3))
+    q8, k8, v8 = (torch.empty((T, H, HEAD_DIM), dtype=torch.uint8, device=DEV) for _ in range(3))
+    out = torch.empty((T, H, HEAD_DIM), dtype=torch.bfloat16, device=DEV)
+    cu = cu_seqlens_tensor(seqlens, DEV)
+
+    def forward(st, q, k, v, c8, o):
+        qfa.quantize_qkv(st, mode, q, k, v, *c8)
+        qfa.fp8_varlen_attn_split_noalloc(*c8, qfa.descale(st), cu, H, out=o)
+
+    forward(qfa.init_scale_state(DEV), qs, ks, vs, (q8, k8, v8), out)   # kernels loaded, workspace address looked up
+    torch.cuda.synchronize()
+    gst, est = qfa.init_scale_state(DEV), qfa.init_scale_state(DEV)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        forward(gst, qs, ks, vs, (q8, k8, v8), out)
+    torch.cuda.synchronize()
+    e8 = tuple(torch.empty_like(q8) for _ in range(3))
+    eout = torch.empty_like(out)
+    for r in range(5):
+        wq = tuple(x[:, :H].contiguous() for x in make_qkv(w, r, device=DEV, num_tokens=T))
+        for dst, src in zip((qs, ks, vs), wq):
+            dst.copy_(src)
+        graph.replay()
+        torch.cuda.synchronize()
+        forward(est, *wq, e8, eout)                                    # eager work on the same workspace
+        torch.cuda.synchronize()
+        for g, e in zip((q8, k8, v8), e8):
+            assert torch.equal(g, e), r
+        assert torch.equal(out.view(torch.int16), eout.view(torch.int16)), r
+        # and the split merge equals the unsplit kernel on these codes to the FP8 kernel's rounding
+        ref = qfa.fp8_varlen_attn(*e8, qfa.descale(est), cu, H)
+        torch.cuda.synchronize()
+        assert (out.float() - ref.float()).abs().max().item() <= 2e-2 * max(1.0, ref.float().abs().max().item()), r
+    log("  5 replays bit-identical to eager")
