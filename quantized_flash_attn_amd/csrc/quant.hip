@@ -103,9 +103,13 @@ __device__ inline uint32_t max_abs_bits(u32x4 w, uint32_t m) {
 __device__ inline float ring_max_others(const DeviceState* st, int t, int cursor) {
     const int hist = st->history_len;
     const int slot = cursor % hist;
+    float r[QFA_MAX_HISTORY];   // every slot at once: one load, no chain of dependent loads
+#pragma unroll
+    for (int j = 0; j < QFA_MAX_HISTORY; ++j) r[j] = st->ring[t][j];
     float m = 0.0f;
-    for (int j = 0; j < hist; ++j)
-        if (j != slot) m = fmaxf(m, st->ring[t][j]);
+#pragma unroll
+    for (int j = 0; j < QFA_MAX_HISTORY; ++j)
+        if (j < hist && j != slot) m = fmaxf(m, r[j]);
     return m;
 }
 
@@ -132,10 +136,11 @@ __device__ float dynamic_inv(DeviceState* st, int t, int n_partials, bool* again
 #pragma unroll
     for (int r = 0; r < kPerThread; ++r) v[r] = st->partial[t][min((int)threadIdx.x + kThreads * r, n_partials - 1)];
     // Ring slots other than the one being replaced, one per lane.
+    const float ring_lane = st->ring[t][lane & (QFA_MAX_HISTORY - 1)];   // loaded alongside cursor and history
     const int cursor = st->cursor_snap;
     const int hist = st->history_len;
     const int slot = cursor % hist;
-    const float rv = (lane < hist && lane != slot) ? st->ring[t][lane] : 0.0f;
+    const float rv = (lane < hist && lane != slot) ? ring_lane : 0.0f;
     uint32_t m = 0;
 #pragma unroll
     for (int r = 0; r < kPerThread; ++r) m = max(m, v[r]);
@@ -227,13 +232,30 @@ struct PackedIO {
 };
 
 // Grid-stride pass over this workgroup's chunks with four chunks in flight
-// per thread: codes with factor inv and, if kMax, the running max|x| bits.
-template <bool kMax, class IO>
-__device__ inline uint32_t stream_pass(const IO& io, float inv) {
+// per thread: codes with factor get_inv() and, if kMax, the running max|x|
+// bits.  The first four loads are issued before get_inv() runs, so a scale
+// derived from the state overlaps the first memory round trip.
+template <bool kMax, class IO, class InvFn>
+__device__ inline uint32_t stream_pass(const IO& io, InvFn get_inv) {
     const int64_t n = io.n();
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     uint32_t m = 0;
+    const bool first_full = i + 3 * stride < n;
+    u32x4 x0[4];
+    if (first_full) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x0[r] = io.load(i + r * stride);
+    }
+    const float inv = get_inv();
+    if (first_full) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if constexpr (kMax) m = max_abs_bits(x0[r], m);
+            io.store(i + r * stride, quantize8(x0[r], inv));
+        }
+        i += 4 * stride;
+    }
     for (; i + 3 * stride < n; i += 4 * stride) {
         u32x4 x[4];
 #pragma unroll
@@ -273,9 +295,11 @@ template <class IO>
 __device__ inline void amax_quantize(DeviceState* st, const IO& io) {
     const int t = blockIdx.y;
     const int cursor = st->cursor;
-    float d, inv;
-    scales_from_amax(ring_max_others(st, t, cursor), &d, &inv);
-    const uint32_t m = stream_pass<true>(io, inv);
+    const uint32_t m = stream_pass<true>(io, [&] {
+        float d, inv;
+        scales_from_amax(ring_max_others(st, t, cursor), &d, &inv);
+        return inv;
+    });
     if (blockIdx.x == 0 && t == 0 && threadIdx.x == 0) st->cursor_snap = cursor;
     store_partial(st, t, m);
 }
@@ -286,7 +310,7 @@ template <class IO>
 __device__ inline void requantize(DeviceState* st, const IO& io, int n_partials) {
     bool again;
     const float inv = dynamic_inv(st, blockIdx.y, n_partials, &again);
-    if (again) stream_pass<false>(io, inv);
+    if (again) stream_pass<false>(io, [=] { return inv; });
 }
 
 // The static factors do not depend on the data: workgroup 0 records them;
@@ -336,8 +360,7 @@ __global__ __launch_bounds__(kThreads) void quantize_static_kernel(DeviceState* 
                                                                    const u32x4* __restrict__ v, int64_t n_chunks,
                                                                    u32x2* __restrict__ q8, u32x2* __restrict__ k8,
                                                                    u32x2* __restrict__ v8) {
-    const float inv = static_inv(st, blockIdx.y);
-    stream_pass<false>(split_io(q, k, v, q8, k8, v8, n_chunks), inv);
+    stream_pass<false>(split_io(q, k, v, q8, k8, v8, n_chunks), [&] { return static_inv(st, blockIdx.y); });
 }
 
 __global__ __launch_bounds__(kThreads) void amax_quantize_packed_kernel(DeviceState* st, const u32x4* __restrict__ qkv,
@@ -362,8 +385,8 @@ __global__ __launch_bounds__(kThreads) void quantize_static_packed_kernel(Device
                                                                           uint32_t cph, u32x2* __restrict__ q8,
                                                                           u32x2* __restrict__ k8,
                                                                           u32x2* __restrict__ v8) {
-    const float inv = static_inv(st, blockIdx.y);
-    stream_pass<false>(packed_io(qkv, q8, k8, v8, out_chunks, num_heads, cph), inv);
+    stream_pass<false>(packed_io(qkv, q8, k8, v8, out_chunks, num_heads, cph),
+                       [&] { return static_inv(st, blockIdx.y); });
 }
 
 int grid_for(int64_t n_chunks, int64_t chunks_per_thread, int cap) {
