@@ -409,9 +409,10 @@ hipError_t launch_quantize_dynamic(DeviceState* st, const uint16_t* q, const uin
     const int64_t chunks = n / 8;
     // One partial per first-pass workgroup (at most kMaxPartials per tensor,
     // each thread streaming >= 8 chunks).  The second pass uses the same grid:
-    // a smaller one costs the same when it only derives the scale (about 2.5 us
-    // at 1 x 8192 tokens, 16 heads) and streams slower when it quantizes again
-    // (53 us with 256 workgroups per tensor, 60 with 64, 83 with 32).
+    // a smaller one costs the same when it only derives the scale (about 4 us
+    // at 1 x 8192 tokens, 16 heads, most of it the launch and one round trip
+    // to the partials) and streams slower when it quantizes again (53 us with
+    // 256 workgroups per tensor, 60 with 64, 83 with 32).
     const int g = grid_for(chunks, 8, kMaxPartials);
     amax_quantize_kernel<<<dim3(g, 3), kThreads, 0, s>>>(st, (const u32x4*)q, (const u32x4*)k, (const u32x4*)v, chunks,
                                                          (u32x2*)q8, (u32x2*)k8, (u32x2*)v8);
