@@ -448,7 +448,9 @@ hipError_t launch_quantize_packed(DeviceState* st, bool dynamic, const uint16_t*
 hipError_t launch_quantize_static(DeviceState* st, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                   int64_t n, uint8_t* q8, uint8_t* k8, uint8_t* v8, hipStream_t s) {
     const int64_t chunks = n / 8;
-    const int g = grid_for(chunks, 16, 2048);
+    // 4 chunks per thread: small tensors get enough workgroups to cover the memory latency (a 2304-token, 16-head
+    // static forward: 8.1 us against 8.9 us with 16); large ones reach the 2048 cap either way
+    const int g = grid_for(chunks, 4, 2048);
     quantize_static_kernel<<<dim3(g, 3), kThreads, 0, s>>>(st, (const u32x4*)q, (const u32x4*)k, (const u32x4*)v,
                                                            chunks, (u32x2*)q8, (u32x2*)k8, (u32x2*)v8);
     return hipGetLastError();
