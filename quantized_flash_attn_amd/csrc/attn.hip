@@ -336,9 +336,9 @@ __device__ __forceinline__ void key_loop(Wave<kDB>& w, unsigned char* smem) {
                 mfma_phase_begin();
                 pv_tile_t<kDB>(smem + kLdsV + prev * kTileBytes, w.vt_rd, pop, w.o);
                 row_sums(pop, w.l);
-                mfma_phase_end();
             }
             if (t >= 1 && t < nt) w.convert_v(smem, cur);
+            mfma_phase_end();
         }
         wait_async_loads();
         __syncthreads();
@@ -363,9 +363,9 @@ __device__ __forceinline__ void key_loop(Wave<kDB>& w, unsigned char* smem) {
                 mfma_phase_begin();
                 pv_tile_t<kDB>(smem + kLdsV + cur * kTileBytes, w.vt_rd, pop, w.o);
                 row_sums(pop, w.l);
-                mfma_phase_end();
             }
             if (t + 1 < nt) w.convert_k(smem, prev);
+            mfma_phase_end();
         } else {
             if (t < nt) softmax_head<kSplit>(w, s, nk_t);
         }
