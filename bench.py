@@ -57,6 +57,10 @@ def parse():
     p.add_argument("--all-configs", action="store_true",
                    help="instead of the benchmark, time every workload (quantize in its own mode, FP8 attention, the "
                         "BF16 baseline); one JSON line per workload")
+    p.add_argument("--seq-sweep", action="store_true",
+                   help="instead of the benchmark, time single images of 2304, 4096, 8192 and 16384 tokens x 16 heads "
+                        "(the kernel-benchmark recipe): FP8 step incl. quantize on the path the library picks, and "
+                        "the BF16 baseline, next to the MI300X figures the pages give for those lengths")
     p.add_argument("--packed-head-dim", type=int, default=0,
                    help="instead of the benchmark, time the fused-QKV path at this head dim (8..128, step 8): "
                         "quantize from [T, 3, H, D] to padded codes, then FP8 attention writing [T, H, D]")
@@ -150,6 +154,76 @@ def all_configs(steps, warmup, prewarm_s):
             "fp8_split_attention": split,
             "launches": n}}), flush=True)
         del sets, codes, out
+        torch.cuda.empty_cache()
+
+
+SWEEP_SEQLENS = (2304, 4096, 8192, 16384)
+
+
+def seq_sweep(steps, warmup, prewarm_s):
+    """Single images of the lengths in "FP8 vision encoder attention", Expected performance, drawn with the
+    kernel-benchmark workload's recipe (16 heads, per-head sigma, 0.1 % x20 outliers), dynamic scaling.  The FP8
+    step is quantize + the attention the library picks (the split-key launch where the automatic count is above
+    1); each loop rotates over input sets whose total exceeds the 256 MB cache and starts after a short untimed
+    run of its own."""
+    import torch
+
+    import quantized_flash_attn_amd as qfa
+    from workloads import WORKLOADS, cu_seqlens_tensor, make_qkv
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    w = WORKLOADS[3]
+    H = w.num_heads
+    mi300x = CONTEXT["incl_fp8_quantization_ms"]["MI300X (AITER)"]
+
+    def timed(fn, n):
+        prewarm(fn, prewarm_s)
+        for i in range(warmup):
+            fn(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    for T in SWEEP_SEQLENS:
+        n_sets = max(2, min(8, (400 << 20) // (3 * T * H * 128 * 2) + 1))
+        sets = [make_qkv(w, f, device=dev, num_tokens=T) for f in range(n_sets)]
+        c8 = [tuple(torch.empty((T, H, 128), dtype=torch.uint8, device=dev) for _ in range(3)) for _ in range(n_sets)]
+        out = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
+        cu = cu_seqlens_tensor([T], dev)
+        st = qfa.init_scale_state(dev)
+        sc = qfa.descale(st)
+        splits = qfa.fp8_varlen_attn_auto_splits(1, T, H)
+        ws = None
+        if splits > 1:
+            ws = torch.empty(qfa.fp8_varlen_attn_workspace_bytes(1, T, H, splits), dtype=torch.uint8, device=dev)
+
+        def fp8_step(i):
+            c = c8[i % n_sets]
+            qfa.quantize_qkv(st, "dynamic", *sets[i % n_sets], *c)
+            if ws is None:
+                qfa.fp8_varlen_attn(*c, sc, cu, H, out=out)
+            else:
+                qfa.fp8_varlen_attn_split(*c, sc, cu, H, num_splits=splits, workspace=ws, out=out)
+
+        n = max(5, steps if T <= 8192 else steps // 2)
+        ms_f = timed(fp8_step, n)
+        ms_b = timed(lambda i: qfa.bf16_varlen_attn(*sets[i % n_sets], cu, H, out=out), n)
+        flop = 4 * T * T * H * 128
+        ref = mi300x.get(f"seq_{T}")
+        print(json.dumps({"seq_sweep": {
+            "tokens": T, "num_heads": H, "input_sets": n_sets, "fp8_key_ranges": splits,
+            "fp8_step_incl_quant_ms": round(ms_f, 4), "fp8_step_tflops": round(flop / (ms_f * 1e-3) / 1e12, 1),
+            "bf16_attention_ms": round(ms_b, 4), "fp8_speedup": round(ms_b / ms_f, 3),
+            "context_mi300x_aiter_ms": ref, "context_source": "'FP8 vision encoder attention', Expected performance "
+                                                              "(heads and batch not stated there)"}}), flush=True)
+        del sets, c8, out, ws
         torch.cuda.empty_cache()
 
 
@@ -447,6 +521,9 @@ def main():
         return
     if args.graph_overhead:
         graph_overhead(args.steps)
+        return
+    if args.seq_sweep:
+        seq_sweep(args.steps, args.warmup, args.prewarm_s)
         return
     if args.all_configs:
         all_configs(args.steps, args.warmup, args.prewarm_s)
