@@ -192,7 +192,7 @@ def seq_sweep(steps, warmup, prewarm_s):
         return e0.elapsed_time(e1) / n
 
     for T in SWEEP_SEQLENS:
-        n_sets = max(2, min(8, (400 << 20) // (3 * T * H * 128 * 2) + 1))
+        n_sets = max(2, -(-(600 << 20) // (3 * T * H * 128 * 2)))   # > 600 MiB of bf16 inputs: past the 256 MB cache
         sets = [make_qkv(w, f, device=dev, num_tokens=T) for f in range(n_sets)]
         c8 = [tuple(torch.empty((T, H, 128), dtype=torch.uint8, device=dev) for _ in range(3)) for _ in range(n_sets)]
         out = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
