@@ -82,6 +82,24 @@ def prewarm(fn, seconds):
     return i
 
 
+def timed_loop(fn, n, warmup, prewarm_s, stream):
+    """ms per call of fn(i) over n back-to-back calls, HIP events on `stream`, after prewarm_s seconds of untimed
+    calls (clocks settle, a kernel's first launches in a process run slow) and `warmup` more."""
+    import torch
+
+    prewarm(fn, prewarm_s)
+    for i in range(warmup):
+        fn(i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(n):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
 def all_configs(steps, warmup, prewarm_s):
     """Per-workload times of the path's parts; each loop rotates over input sets totalling more than 600 MiB of
     bf16 (64 sets at most) and starts after a short untimed run of its own (a kernel's first launches in a process,
@@ -96,17 +114,7 @@ def all_configs(steps, warmup, prewarm_s):
     stream = torch.cuda.current_stream(dev)
 
     def timed(fn, n):
-        prewarm(fn, prewarm_s)
-        for i in range(warmup):
-            fn(i)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for i in range(n):
-            fn(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n
+        return timed_loop(fn, n, warmup, prewarm_s, stream)
 
     for wi, w in sorted(WORKLOADS.items()):
         H, T = w.num_heads, w.total_tokens
@@ -182,17 +190,7 @@ def seq_sweep(steps, warmup, prewarm_s):
     mi300x = CONTEXT["incl_fp8_quantization_ms"]["MI300X (AITER)"]
 
     def timed(fn, n):
-        prewarm(fn, prewarm_s)
-        for i in range(warmup):
-            fn(i)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for i in range(n):
-            fn(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n
+        return timed_loop(fn, n, warmup, prewarm_s, stream)
 
     for T in SWEEP_SEQLENS:
         n_sets = max(2, -(-(600 << 20) // (3 * T * H * 128 * 2)))   # > 600 MiB of bf16 inputs: past the 256 MB cache
@@ -258,17 +256,7 @@ def packed_path(head_dim, steps, warmup, prewarm_s):
     sc = qfa.descale(st)
 
     def timed(fn, n):
-        prewarm(fn, prewarm_s)   # clocks settle before each loop, as for the main benchmark
-        for i in range(warmup):
-            fn(i)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for i in range(n):
-            fn(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n
+        return timed_loop(fn, n, warmup, prewarm_s, stream)
 
     def unfused(i):
         x = sets[i % len(sets)]
