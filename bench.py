@@ -61,6 +61,10 @@ def parse():
                    help="instead of the benchmark, time single images of 2304, 4096, 8192 and 16384 tokens x 16 heads "
                         "(the kernel-benchmark recipe): FP8 step incl. quantize on the path the library picks, and "
                         "the BF16 baseline, next to the MI300X figures the pages give for those lengths")
+    p.add_argument("--split-sweep", action="store_true",
+                   help="instead of the benchmark, time the split-key attention on launches that leave CUs idle "
+                        "(1 x 2304 tokens x 8 heads, 1 x 4608 x 4, 1 x 9216 x 2, 1 x 2304 x 16) for 1, 2, 3 and 6 key "
+                        "ranges and the automatic count")
     p.add_argument("--packed-head-dim", type=int, default=0,
                    help="instead of the benchmark, time the fused-QKV path at this head dim (8..128, step 8): "
                         "quantize from [T, 3, H, D] to padded codes, then FP8 attention writing [T, H, D]")
@@ -225,6 +229,44 @@ def seq_sweep(steps, warmup, prewarm_s):
             "context_mi300x_aiter_ms": ref, "context_source": "'FP8 vision encoder attention', Expected performance "
                                                               "(heads and batch not stated there)"}}), flush=True)
         del sets, c8, out, ws
+        torch.cuda.empty_cache()
+
+
+SPLIT_SHAPES = ((2304, 8), (4608, 4), (9216, 2), (2304, 16))
+
+
+def split_sweep(steps, warmup, prewarm_s):
+    """Attention alone (split kernel + merge, or the unsplit kernel for one range) on single images whose
+    (head, query tile) pairs fill few of the 256 CUs, kernel-benchmark recipe, codes of one dynamic forward.  The
+    workspace is allocated once per shape, outside the timed loops."""
+    import torch
+
+    import quantized_flash_attn_amd as qfa
+    from workloads import WORKLOADS, cu_seqlens_tensor, make_qkv
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    base = WORKLOADS[3]
+    for T, H in SPLIT_SHAPES:
+        q, k, v = (x[:, :H].contiguous() for x in make_qkv(base, 0, device=dev, num_tokens=T))
+        st = qfa.init_scale_state(dev)
+        q8, k8, v8 = qfa.quantize_qkv(st, "dynamic", q, k, v)
+        sc = qfa.descale(st)
+        cu = cu_seqlens_tensor([T], dev)
+        out = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
+        auto = qfa.fp8_varlen_attn_auto_splits(1, T, H)
+        ws = torch.empty(max(256, qfa.fp8_varlen_attn_workspace_bytes(1, T, H, 6)), dtype=torch.uint8, device=dev)
+        flop = 4 * T * T * H * 128
+        res = {}
+        for S in (1, 2, 3, 6):
+            ms = timed_loop(lambda i: qfa.fp8_varlen_attn_split(q8, k8, v8, sc, cu, H, num_splits=S, workspace=ws,
+                                                                out=out), steps, warmup, prewarm_s, stream)
+            res[str(S)] = {"us": round(ms * 1e3, 2), "tflops": round(flop / (ms * 1e-3) / 1e12, 1)}
+        query_tiles = (T // 256 + (1 if T % 256 else 0)) * H
+        print(json.dumps({"split_sweep": {"tokens": T, "num_heads": H, "query_tiles": query_tiles,
+                                          "auto_key_ranges": auto, "by_key_ranges": res}}), flush=True)
+        del q, k, v, q8, k8, v8, out, ws
         torch.cuda.empty_cache()
 
 
@@ -512,6 +554,9 @@ def main():
         return
     if args.graph_overhead:
         graph_overhead(args.steps)
+        return
+    if args.split_sweep:
+        split_sweep(args.steps, args.warmup, args.prewarm_s)
         return
     if args.seq_sweep:
         seq_sweep(args.steps, args.warmup, args.prewarm_s)
