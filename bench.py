@@ -65,6 +65,11 @@ def parse():
                    help="instead of the benchmark, time the split-key attention on launches that leave CUs idle "
                         "(1 x 2304 tokens x 8 heads, 1 x 4608 x 4, 1 x 9216 x 2, 1 x 2304 x 16) for 1, 2, 3 and 6 key "
                         "ranges and the automatic count")
+    p.add_argument("--power", action="store_true",
+                   help="instead of the benchmark, run the FP8 attention, the FP8 step, the BF16 baseline and a "
+                        "full-chip MFMA throughput kernel (f16, bf16, fp8) back to back for --power-s seconds each, "
+                        "reading socket power and GFX clocks with amd-smi meanwhile; one JSON line per item")
+    p.add_argument("--power-s", type=float, default=4.0)
     p.add_argument("--packed-head-dim", type=int, default=0,
                    help="instead of the benchmark, time the fused-QKV path at this head dim (8..128, step 8): "
                         "quantize from [T, 3, H, D] to padded codes, then FP8 attention writing [T, H, D]")
@@ -508,6 +513,141 @@ def as_specified(w, qfa, torch, cu, out, stream):
     }
 
 
+def smi_sample():
+    """(socket power in W, [GFX clock per XCD in MHz]) from `amd-smi metric -g 0 -p -c`, or None."""
+    import subprocess
+
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-p", "-c"], stdout=subprocess.PIPE,
+                           stderr=subprocess.STDOUT, text=True, timeout=30)
+    except (OSError, subprocess.TimeoutExpired):
+        return None
+    power, clks, sec = None, [], ""
+    for line in r.stdout.splitlines():
+        t = line.strip()
+        if t.startswith("SOCKET_POWER:"):
+            try:
+                power = float(t.split()[1])
+            except (IndexError, ValueError):
+                pass
+        elif t.endswith(":") and " " not in t:
+            sec = t[:-1]
+        elif t.startswith("CLK:") and sec.startswith("GFX_"):
+            try:
+                clks.append(float(t.split()[1]))
+            except (IndexError, ValueError):
+                pass
+    return (power, clks) if power is not None or clks else None
+
+
+def sustained(fn, seconds, stream):
+    """Run fn(i) back to back for `seconds` (after 0.3 s untimed), reading amd-smi at 40 % and 70 % of the run.
+    Returns (ms per call, calls, [samples])."""
+    import threading
+
+    import torch
+
+    samples = []
+    stop = threading.Event()
+
+    def sampler():
+        for wait in (0.4 * seconds, 0.3 * seconds):
+            if stop.wait(wait):
+                return
+            got = smi_sample()
+            if got:
+                samples.append(got)
+
+    prewarm(fn, 0.3)
+    th = threading.Thread(target=sampler)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    th.start()
+    e0.record(stream)
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            fn(n)
+            n += 1
+        torch.cuda.synchronize()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    return e0.elapsed_time(e1) / n, n, samples
+
+
+def power_profile(seconds):
+    """Sustained rates at the board's power limit: the path's kernels and a full-chip matrix-throughput kernel
+    (tests/hw/mfma_probe.hip, mfma_burn) run back to back, with socket power and GFX clocks read meanwhile."""
+    import ctypes
+
+    import torch
+
+    import quantized_flash_attn_amd as qfa
+    from workloads import WORKLOADS, cu_seqlens_tensor, make_qkv
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    w = WORKLOADS[3]
+    H, T = w.num_heads, w.total_tokens
+    sets = [make_qkv(w, i, device=dev) for i in range(4)]
+    q8 = torch.empty((T, H, 128), dtype=torch.uint8, device=dev)
+    k8, v8 = torch.empty_like(q8), torch.empty_like(q8)
+    out = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
+    cu = cu_seqlens_tensor(w.seqlens, dev)
+    st = qfa.init_scale_state(dev)
+    scales = qfa.descale(st)
+    qfa.quantize_qkv(st, "dynamic", *sets[0], q8, k8, v8)
+
+    def report(item, ms, n, samples, flop, extra=None):
+        pw = [p for p, _ in samples if p is not None]
+        ck = [c for _, cl in samples for c in cl]
+        power = sum(pw) / len(pw) if pw else None
+        rec = {"power_item": item, "seconds": seconds, "calls": n, "ms": round(ms, 4),
+               "tflops": round(flop / (ms * 1e-3) / 1e12, 1),
+               "socket_power_w": round(power, 1) if power else None,
+               "gfx_clock_mhz_mean": round(sum(ck) / len(ck), 0) if ck else None,
+               "gfx_clock_mhz_range": [min(ck), max(ck)] if ck else None,
+               "energy_j_per_call": round(power * ms * 1e-3, 4) if power else None,
+               "smi_samples": len(samples)}
+        rec.update(extra or {})
+        print(json.dumps(rec), flush=True)
+
+    flop = w.attn_flop
+    ms, n, smp = sustained(lambda i: qfa.fp8_varlen_attn(q8, k8, v8, scales, cu, H, out=out), seconds, stream)
+    report("fp8_attention " + w.name, ms, n, smp, flop)
+
+    def step(i):
+        qfa.quantize_qkv(st, "dynamic", *sets[i % len(sets)], q8, k8, v8)
+        qfa.fp8_varlen_attn(q8, k8, v8, scales, cu, H, out=out)
+
+    ms, n, smp = sustained(step, seconds, stream)
+    report("fp8_step_incl_quantize " + w.name, ms, n, smp, flop)
+    ms, n, smp = sustained(lambda i: qfa.bf16_varlen_attn(*sets[i % len(sets)], cu, H, out=out), seconds, stream)
+    report("bf16_attention " + w.name, ms, n, smp, flop)
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "tests", "hw", "libmfma_probe.so"))
+    lib.mfma_burn.restype = ctypes.c_int
+    lib.mfma_burn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                              ctypes.c_void_p]
+    grid = 2 * torch.cuda.get_device_properties(dev).multi_processor_count
+    bout = torch.empty(grid * 256, dtype=torch.float32, device=dev)
+    cyc = torch.zeros(grid, dtype=torch.int64, device=dev)
+    # kind, name, flop per instruction, rounds (about 20 ms per launch)
+    for kind, name, fpi, rounds in ((0, "f16 16x16x32", 16 * 16 * 32 * 2, 1 << 18),
+                                    (2, "bf16 16x16x32", 16 * 16 * 32 * 2, 1 << 18),
+                                    (1, "fp8 16x16x128", 16 * 16 * 128 * 2, 1 << 17)):
+        def burn(i, kind=kind, rounds=rounds):
+            assert lib.mfma_burn(kind, grid, rounds, bout.data_ptr(), cyc.data_ptr(), stream.cuda_stream) == 0
+
+        ms, n, smp = sustained(burn, seconds, stream)
+        ticks = float(cyc.double().mean())
+        report("mfma_burn " + name, ms, n, smp, grid * 4 * rounds * 4 * fpi,
+               {"workgroups": grid, "shader_clock_mhz_from_s_memtime": round(ticks / (ms * 1e3), 0)})
+
+
 def make_set(w, f, torch):
     from workloads import make_qkv
 
@@ -566,6 +706,9 @@ def main():
         return
     if args.packed_head_dim:
         packed_path(args.packed_head_dim, args.steps, args.warmup, args.prewarm_s)
+        return
+    if args.power:
+        power_profile(args.power_s)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "the path runs on one GPU (sharding across GPUs is a design only); --gpus must be 1"}))

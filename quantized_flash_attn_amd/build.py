@@ -52,7 +52,10 @@ def _run(cmd, verbose):
 
 
 # Test infrastructure built alongside the library: a one-wave probe of the
-# matrix instructions' summation (tests/test_gpu_mfma_hw.py loads it).
+# matrix instructions' summation (tests/test_gpu_mfma_hw.py loads it), and a
+# full-chip matrix-throughput kernel (bench.py --power).  Its matrix
+# instructions write their accumulators to ordinary VGPRs, so the throughput
+# loop carries no accumulator copies.
 PROBE_SRC = os.path.join(ROOT, "tests", "hw", "mfma_probe.hip")
 PROBE_LIB = os.path.join(ROOT, "tests", "hw", "libmfma_probe.so")
 
@@ -62,7 +65,7 @@ def build_probe(verbose: bool = True) -> str:
     cc = hipcc()
     with tempfile.TemporaryDirectory(prefix="qfa_probe_") as tmp:
         out = os.path.join(tmp, "libmfma_probe.so")
-        _run([cc, *HIPCC_FLAGS, "-shared", PROBE_SRC, "-o", out], verbose)
+        _run([cc, *HIPCC_FLAGS, "-mllvm", "-amdgpu-mfma-vgpr-form=1", "-shared", PROBE_SRC, "-o", out], verbose)
         shutil.copyfile(out, PROBE_LIB + ".tmp")
         os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
     return PROBE_LIB
