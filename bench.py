@@ -513,12 +513,42 @@ def as_specified(w, qfa, torch, cu, out, stream):
     }
 
 
-def smi_sample():
-    """(socket power in W, [GFX clock per XCD in MHz]) from `amd-smi metric -g 0 -p -c`, or None."""
+def smi_gpu(dev):
+    """(amd-smi index, BDF) of the GPU torch runs on, matched by PCI domain and bus; (None, None) if no match."""
+    import subprocess
+
+    import torch
+
+    prop = torch.cuda.get_device_properties(dev)
+    try:
+        r = subprocess.run(["amd-smi", "list"], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True, timeout=30)
+    except (OSError, subprocess.TimeoutExpired):
+        return None, None
+    idx = None
+    for line in r.stdout.splitlines():
+        t = line.strip()
+        if t.startswith("GPU:"):
+            try:
+                idx = int(t.split()[1])
+            except (IndexError, ValueError):
+                idx = None
+        elif t.startswith("BDF:") and idx is not None:
+            bdf = t.split()[1]
+            try:
+                dom, bus = int(bdf.split(":")[0], 16), int(bdf.split(":")[1], 16)
+            except (IndexError, ValueError):
+                continue
+            if dom == prop.pci_domain_id and bus == prop.pci_bus_id:
+                return idx, bdf
+    return None, None
+
+
+def smi_sample(gpu):
+    """(socket power in W, [GFX clock per XCD in MHz]) from `amd-smi metric -g gpu -p -c`, or None."""
     import subprocess
 
     try:
-        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-p", "-c"], stdout=subprocess.PIPE,
+        r = subprocess.run(["amd-smi", "metric", "-g", str(gpu), "-p", "-c"], stdout=subprocess.PIPE,
                            stderr=subprocess.STDOUT, text=True, timeout=30)
     except (OSError, subprocess.TimeoutExpired):
         return None
@@ -540,9 +570,9 @@ def smi_sample():
     return (power, clks) if power is not None or clks else None
 
 
-def sustained(fn, seconds, stream):
-    """Run fn(i) back to back for `seconds` (after 0.3 s untimed), reading amd-smi at 40 % and 70 % of the run.
-    Returns (ms per call, calls, [samples])."""
+def sustained(fn, seconds, stream, gpu):
+    """Run fn(i) back to back for `seconds` (after 0.3 s untimed), reading amd-smi (GPU index `gpu`, or nothing if
+    None) at 40 % and 70 % of the run.  Returns (ms per call, calls, [samples])."""
     import threading
 
     import torch
@@ -552,9 +582,9 @@ def sustained(fn, seconds, stream):
 
     def sampler():
         for wait in (0.4 * seconds, 0.3 * seconds):
-            if stop.wait(wait):
+            if gpu is None or stop.wait(wait):
                 return
-            got = smi_sample()
+            got = smi_sample(gpu)
             if got:
                 samples.append(got)
 
@@ -600,6 +630,7 @@ def power_profile(seconds):
     st = qfa.init_scale_state(dev)
     scales = qfa.descale(st)
     qfa.quantize_qkv(st, "dynamic", *sets[0], q8, k8, v8)
+    gpu, bdf = smi_gpu(dev)   # the sensors of the GPU this process runs on
 
     def report(item, ms, n, samples, flop, extra=None):
         pw = [p for p, _ in samples if p is not None]
@@ -611,21 +642,22 @@ def power_profile(seconds):
                "gfx_clock_mhz_mean": round(sum(ck) / len(ck), 0) if ck else None,
                "gfx_clock_mhz_range": [min(ck), max(ck)] if ck else None,
                "energy_j_per_call": round(power * ms * 1e-3, 4) if power else None,
-               "smi_samples": len(samples)}
+               "smi_samples": len(samples), "smi_gpu": gpu, "smi_bdf": bdf}
         rec.update(extra or {})
         print(json.dumps(rec), flush=True)
 
     flop = w.attn_flop
-    ms, n, smp = sustained(lambda i: qfa.fp8_varlen_attn(q8, k8, v8, scales, cu, H, out=out), seconds, stream)
+    ms, n, smp = sustained(lambda i: qfa.fp8_varlen_attn(q8, k8, v8, scales, cu, H, out=out), seconds, stream, gpu)
     report("fp8_attention " + w.name, ms, n, smp, flop)
 
     def step(i):
         qfa.quantize_qkv(st, "dynamic", *sets[i % len(sets)], q8, k8, v8)
         qfa.fp8_varlen_attn(q8, k8, v8, scales, cu, H, out=out)
 
-    ms, n, smp = sustained(step, seconds, stream)
+    ms, n, smp = sustained(step, seconds, stream, gpu)
     report("fp8_step_incl_quantize " + w.name, ms, n, smp, flop)
-    ms, n, smp = sustained(lambda i: qfa.bf16_varlen_attn(*sets[i % len(sets)], cu, H, out=out), seconds, stream)
+    ms, n, smp = sustained(lambda i: qfa.bf16_varlen_attn(*sets[i % len(sets)], cu, H, out=out), seconds, stream,
+                           gpu)
     report("bf16_attention " + w.name, ms, n, smp, flop)
 
     lib = ctypes.CDLL(os.path.join(ROOT, "tests", "hw", "libmfma_probe.so"))
@@ -642,7 +674,7 @@ def power_profile(seconds):
         def burn(i, kind=kind, rounds=rounds):
             assert lib.mfma_burn(kind, grid, rounds, bout.data_ptr(), cyc.data_ptr(), stream.cuda_stream) == 0
 
-        ms, n, smp = sustained(burn, seconds, stream)
+        ms, n, smp = sustained(burn, seconds, stream, gpu)
         ticks = float(cyc.double().mean())
         report("mfma_burn " + name, ms, n, smp, grid * 4 * rounds * 4 * fpi,
                {"workgroups": grid, "shader_clock_mhz_from_s_memtime": round(ticks / (ms * 1e3), 0)})
