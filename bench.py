@@ -47,7 +47,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-as-specified", action="store_true",
                    help="skip the workload timed as its recipe states it (fresh state, its own 16 distinct forwards)")
-    p.add_argument("--cpu-rows", type=int, default=256, help="query rows of the oracle's attention sample")
+    p.add_argument("--cpu-rows", type=int, default=0,
+                   help="query rows of the oracle's attention sample (0: every row of the first sequence)")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="instead of the benchmark, time a plain device copy of this many MiB (the known-size "
                         "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -70,6 +71,8 @@ def parse():
                         "full-chip MFMA throughput kernel (f16, bf16, fp8) back to back for --power-s seconds each, "
                         "reading socket power and GFX clocks with amd-smi meanwhile; one JSON line per item")
     p.add_argument("--power-s", type=float, default=4.0)
+    p.add_argument("--no-power-limited", action="store_true",
+                   help="skip the 2 s sustained attention and matrix-throughput runs of the power_limited block")
     p.add_argument("--packed-head-dim", type=int, default=0,
                    help="instead of the benchmark, time the fused-QKV path at this head dim (8..128, step 8): "
                         "quantize from [T, 3, H, D] to padded codes, then FP8 attention writing [T, H, D]")
@@ -428,15 +431,15 @@ def cpu_baseline(w, xs_host, descale_inv, rows):
     cores = len(os.sched_getaffinity(0))
     q, k, v = xs_host
     inv = descale_inv[1]
-    # quantize sample: 1/16 of Q (amax + encode), extrapolated to Q, K and V
-    n_total = 3 * q.size
-    sample = q.reshape(-1)[: q.size // 16]
+    # quantize: amax + encode of Q, K and V in full
     t0 = time.perf_counter()
-    oracle.amax(sample)
-    oracle.quantize(sample, inv[0])
-    t_q = (time.perf_counter() - t0) * n_total / sample.size
-    # attention sample: `rows` query rows of sequence 0 (all heads), oracle's own codes
+    for t, x in enumerate((q, k, v)):
+        oracle.amax(x)
+        oracle.quantize(x, inv[t])
+    t_q = time.perf_counter() - t0
+    # attention sample: `rows` query rows of sequence 0 (all of them when rows is 0; all heads), oracle's own codes
     T = w.seqlens[0]
+    rows = T if rows <= 0 or rows > T else rows
     q8 = oracle.quantize(q[:T], inv[0])
     k8 = oracle.quantize(k[:T], inv[1])
     v8 = oracle.quantize(v[:T], inv[2])
@@ -452,9 +455,10 @@ def cpu_baseline(w, xs_host, descale_inv, rows):
         "cores": blas_threads or cores,
         "cores_available": cores,
         "kind": "oracle",
-        "sample": f"amax+encode of {sample.size} elements (1/16 of Q) and float64 attention of {rows} query rows x "
-                  f"{w.num_heads} heads x {T} keys; extrapolated to the full workload "
-                  f"(quantize {t_q:.2f} s + attention {t_a:.1f} s per step)",
+        "sample": f"amax+encode of Q, K and V in full ({3 * q.size} elements) and float64 attention of {rows} query "
+                  f"rows x {w.num_heads} heads x {T} keys of the first sequence"
+                  + ("" if rows * T == sum(n * n for n in w.seqlens) else ", extrapolated to the full workload")
+                  + f" (quantize {t_q:.2f} s + attention {t_a:.1f} s per step)",
     }
 
 
@@ -610,8 +614,6 @@ def sustained(fn, seconds, stream, gpu):
 def power_profile(seconds):
     """Sustained rates at the board's power limit: the path's kernels and a full-chip matrix-throughput kernel
     (tests/hw/mfma_probe.hip, mfma_burn) run back to back, with socket power and GFX clocks read meanwhile."""
-    import ctypes
-
     import torch
 
     import quantized_flash_attn_amd as qfa
@@ -633,13 +635,12 @@ def power_profile(seconds):
     gpu, bdf = smi_gpu(dev)   # the sensors of the GPU this process runs on
 
     def report(item, ms, n, samples, flop, extra=None):
-        pw = [p for p, _ in samples if p is not None]
         ck = [c for _, cl in samples for c in cl]
-        power = sum(pw) / len(pw) if pw else None
+        power, clock = smi_means(samples)
         rec = {"power_item": item, "seconds": seconds, "calls": n, "ms": round(ms, 4),
                "tflops": round(flop / (ms * 1e-3) / 1e12, 1),
                "socket_power_w": round(power, 1) if power else None,
-               "gfx_clock_mhz_mean": round(sum(ck) / len(ck), 0) if ck else None,
+               "gfx_clock_mhz_mean": round(clock, 0) if clock else None,
                "gfx_clock_mhz_range": [min(ck), max(ck)] if ck else None,
                "energy_j_per_call": round(power * ms * 1e-3, 4) if power else None,
                "smi_samples": len(samples), "smi_gpu": gpu, "smi_bdf": bdf}
@@ -660,24 +661,75 @@ def power_profile(seconds):
                            gpu)
     report("bf16_attention " + w.name, ms, n, smp, flop)
 
-    lib = ctypes.CDLL(os.path.join(ROOT, "tests", "hw", "libmfma_probe.so"))
+    for kind in BURN_KINDS:
+        ms, n, smp, flop_burn, extra = mfma_burn_sustained(kind, seconds, stream, gpu)
+        report("mfma_burn " + BURN_KINDS[kind][0], ms, n, smp, flop_burn, extra)
+
+
+# mfma_burn kinds (tests/hw/mfma_probe.hip): name, flop per instruction, rounds per launch (about 20 ms)
+BURN_KINDS = {0: ("f16 16x16x32", 16 * 16 * 32 * 2, 1 << 18),
+              2: ("bf16 16x16x32", 16 * 16 * 32 * 2, 1 << 18),
+              1: ("fp8 16x16x128", 16 * 16 * 128 * 2, 1 << 17)}
+
+
+def mfma_burn_sustained(kind, seconds, stream, gpu):
+    """The full-chip matrix-throughput kernel of the hardware probe library, back to back for `seconds`:
+    (ms per launch, launches, amd-smi samples, flop per launch, extra fields), or None without the library."""
+    import ctypes
+
+    import torch
+
+    path = os.path.join(ROOT, "tests", "hw", "libmfma_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
     lib.mfma_burn.restype = ctypes.c_int
     lib.mfma_burn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                               ctypes.c_void_p]
+    dev = torch.device("cuda", 0)
     grid = 2 * torch.cuda.get_device_properties(dev).multi_processor_count
     bout = torch.empty(grid * 256, dtype=torch.float32, device=dev)
     cyc = torch.zeros(grid, dtype=torch.int64, device=dev)
-    # kind, name, flop per instruction, rounds (about 20 ms per launch)
-    for kind, name, fpi, rounds in ((0, "f16 16x16x32", 16 * 16 * 32 * 2, 1 << 18),
-                                    (2, "bf16 16x16x32", 16 * 16 * 32 * 2, 1 << 18),
-                                    (1, "fp8 16x16x128", 16 * 16 * 128 * 2, 1 << 17)):
-        def burn(i, kind=kind, rounds=rounds):
-            assert lib.mfma_burn(kind, grid, rounds, bout.data_ptr(), cyc.data_ptr(), stream.cuda_stream) == 0
+    _, fpi, rounds = BURN_KINDS[kind]
 
-        ms, n, smp = sustained(burn, seconds, stream, gpu)
-        ticks = float(cyc.double().mean())
-        report("mfma_burn " + name, ms, n, smp, grid * 4 * rounds * 4 * fpi,
-               {"workgroups": grid, "shader_clock_mhz_from_s_memtime": round(ticks / (ms * 1e3), 0)})
+    def burn(i):
+        assert lib.mfma_burn(kind, grid, rounds, bout.data_ptr(), cyc.data_ptr(), stream.cuda_stream) == 0
+
+    ms, n, smp = sustained(burn, seconds, stream, gpu)
+    ticks = float(cyc.double().mean())
+    return ms, n, smp, grid * 4 * rounds * 4 * fpi, {"workgroups": grid,
+                                                      "shader_clock_mhz_from_s_memtime": round(ticks / (ms * 1e3), 0)}
+
+
+def smi_means(samples):
+    """(mean socket power in W, mean GFX clock in MHz) over amd-smi samples; None where nothing was read."""
+    pw = [p for p, _ in samples if p is not None]
+    ck = [c for _, cl in samples for c in cl]
+    return (sum(pw) / len(pw) if pw else None), (sum(ck) / len(ck) if ck else None)
+
+
+def power_limited(fn, flop, seconds, stream):
+    """The attention run back to back for `seconds` with socket power and GFX clock read meanwhile, next to the f16
+    matrix throughput the chip sustains under the same conditions (mfma_burn)."""
+    import torch
+
+    gpu, _ = smi_gpu(torch.device("cuda", 0))
+    ms, n, smp = sustained(fn, seconds, stream, gpu)
+    power, clock = smi_means(smp)
+    tflops = flop / (ms * 1e-3) / 1e12
+    rec = {"seconds": seconds, "attention_ms": round(ms, 4), "attention_tflops": round(tflops, 1),
+           "socket_power_w": round(power, 1) if power else None, "gfx_clock_mhz": round(clock) if clock else None,
+           "energy_j_per_call": round(power * ms * 1e-3, 4) if power else None}
+    burn = mfma_burn_sustained(0, seconds, stream, gpu)
+    if burn is not None:
+        bms, _, bsmp, bflop, _ = burn
+        bpower, bclock = smi_means(bsmp)
+        btf = bflop / (bms * 1e-3) / 1e12
+        rec.update({"mfma_burn_f16_tflops": round(btf, 1),
+                    "mfma_burn_socket_power_w": round(bpower, 1) if bpower else None,
+                    "mfma_burn_gfx_clock_mhz": round(bclock) if bclock else None,
+                    "attention_frac_of_sustained_f16": round(tflops / btf, 4)})
+    return rec
 
 
 def make_set(w, f, torch):
@@ -865,6 +917,9 @@ def main():
     }
     if w.index == 3 and not args.no_as_specified:
         res["as_specified"] = as_specified(w, qfa, torch, cu, out, stream)
+    if not args.no_power_limited:
+        res["power_limited"] = power_limited(lambda i: qfa.fp8_varlen_attn(q8, k8, v8, scales, cu, H, out=out),
+                                             flop, 2.0, stream)
     res["context_other_hardware"] = CONTEXT
     if not args.no_cpu_baseline:
         import oracle
