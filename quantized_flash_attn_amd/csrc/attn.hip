@@ -20,14 +20,14 @@
 //     tiles never cross a cu_seqlens boundary.  Workgroup ids are remapped
 //     so that consecutive tiles (same head, same K/V) land on one XCD and
 //     share its L2.
-//   * Each wave owns 32 queries (two 16-query MFMA blocks) and streams all
-//     keys of the sequence in 128-key tiles staged through LDS.
+//   * Each wave owns 32 queries and streams all keys of the sequence in
+//     128-key tiles staged through LDS.
 //   * K and V tiles of codes are fetched with buffer_load_dwordx4 ... lds (L2
 //     to LDS without registers) into one staging buffer each; rows past the
 //     end of the sequence are outside the buffer descriptor's range and
 //     arrive as zeros (their scores are masked).  Once per tile, a wave group
-//     converts the codes exactly to fp16 right after one of its P V products
-//     (every E4M3 value is an fp16 value) into double-buffered fp16 tiles:
+//     converts the codes exactly to fp16 (every E4M3 value is an fp16 value)
+//     into double-buffered fp16 tiles:
 //     K in the layout of the BF16 baseline kernel (attn_common.h), V
 //     transposed (V^T, read by transposed 8-bit LDS reads of the staged
 //     codes), so that both products read their LDS operands with
@@ -36,13 +36,24 @@
 // Ping-pong schedule.  Waves 0-3 (group A) and 4-7 (group B) share the four
 // SIMDs pairwise.  Each key tile takes four barrier-separated slots, and B
 // runs two slots behind A, so on every SIMD one wave issues MFMAs while the
-// other issues the softmax VALU work; the code conversions follow the P V
-// products, in the slot of the other group's softmax head:
+// other issues the softmax VALU work:
 //            slot 1          slot 2            slot 3          slot 4
-//   A    S_t = K_t Q^T    p_t (head)        p_t (tail)      O += P_t V_t,
-//                                                           K_{t+1} -> fp16
-//   B    p_{t-1} (tail)   O += P V_{t-1},   S_t = K_t Q^T   p_t (head)
-//                         V_t -> fp16 V^T
+//   A    S_t = K_t Q^T    p_t (head)        p_t (tail)      O += P_t V_t
+//   B    p_{t-1} (tail)   O += P V_{t-1}    S_t = K_t Q^T   p_t (head)
+// plus one code conversion of K and one of V per tile (key_loop says where).
+//
+// Two register layouts (the Wave and WaveWide structs below):
+//   16x16   v_mfma_f32_16x16x32_f16, each wave two 16-query blocks; the
+//           conversions follow the P V products.
+//   32x32   v_mfma_f32_32x32x16_f16, each wave one 32-query block: half the
+//           MFMA instructions and waits for the same LDS bytes, and one lane
+//           swap for a row max; the conversions follow the softmax tails.
+// The 32x32 layout needs 4-6 % fewer GPU cycles per tile but about 4 % more
+// energy per call.  A launch that fills the chip holds the board at its
+// power limit, where time is energy over the limit, so it runs the 16x16
+// layout; a launch of at most 3/4 as many workgroups as CUs stays below the
+// limit at full clock, so it runs the 32x32 layout (head dims above 96; the
+// 16x16 layout covers all head dims).
 //
 //   S = K Q^T       fp16 MFMA on the exactly converted codes.  gfx950's fp8
 //                   MFMAs add each group of 8 products on a window of about
@@ -50,25 +61,28 @@
 //                   the rest; with outlier-heavy Q/K that moves dominant
 //                   logits by up to ~0.5 log2 units.  The fp16 MFMA sums
 //                   products of two E4M3 values (at most 8 significant bits)
-//                   in fp32.  The accumulator gives every lane 32 keys of ONE
-//                   query, so the row max is in-lane plus two lane swaps.
+//                   in fp32.  The 16x16 accumulator gives every lane 32 keys
+//                   of ONE query, so the row max is in-lane plus two lane
+//                   swaps (32x32: 64 keys, one swap).
 //   online softmax  p = 2^(S c + 8 - mc), c = s_q s_k log2(e) / sqrt(D), mc
 //                   a running row max (log2 units) that may lag a tile's
 //                   max by 7.5 units and, when it must move, moves 4 units
-//                   above it; the decision is taken per 16-query block, so
-//                   most blocks skip the O and l rescale on most tiles.
+//                   above it; the decision is taken per MFMA query block
+//                   (16 or 32 queries), so most blocks skip the O and l
+//                   rescale on most tiles.
 //   O^T += V^T P^T  fp16 MFMA: A = V^T read with ds_read_b128 from the
 //                   converted V^T, B = P^T straight from the S accumulator
 //                   layout, rounded to fp16 (11 significant bits; bf16's 8
 //                   cost up to 2^-9 of each weight).  Two E4M3 terms of p (hi + lo)
 //                   on the fp8 MFMA would cost the same matrix time plus two
 //                   slow conversions per pair of p; one E4M3 term is too
-//                   coarse.  l is the row sum of the same fp16 p, taken by an
-//                   MFMA with an all-ones A operand (8 per tile, in the
-//                   LDS-bound P V slot, instead of 64 fp32 adds in the VALU
+//                   coarse.  l is the row sum of the same fp16 p, taken by
+//                   16x16x32 MFMAs with a ones (or selector) A operand (8 per
+//                   tile, in the P V slot, instead of 64 fp32 adds in the VALU
 //                   slot), so O / l is a convex combination of V rows.
 //   epilogue        out = bf16(O * s_v / l).
 
+#include <atomic>
 #include <cmath>
 #include <mutex>
 
@@ -116,7 +130,8 @@ __device__ inline f16x8 codes_to_f16x8(uint32_t w0, uint32_t w1) {
 // and ends after the last row of the sequence: rows past it are out of
 // range, which the hardware turns into zeros in LDS.
 __device__ inline void issue_code_tile_load(const uint8_t* __restrict__ src, uint32_t row_stride, int h, int kt,
-                                            int seq_hi, lds_u8* dst, int wave, uint32_t lane_off) {
+                                            int seq_hi, lds_u8* dst, int wave, uint32_t lane_off0,
+                                            uint32_t lane_off1) {
     const int nrows = min(seq_hi - kt, kBN);
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
@@ -125,7 +140,8 @@ __device__ inline void issue_code_tile_load(const uint8_t* __restrict__ src, uin
         const int nrec = rows_left > 0 ? (rows_left - 1) * (int)row_stride + kD : 0;
         const size_t off = (size_t)(kt + seg * 8) * row_stride + (size_t)h * kD;
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)(src + off), 0, nrec, kRsrcWord3);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + seg * 1024, 16, (int)lane_off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + seg * 1024, 16, (int)(r == 0 ? lane_off0 : lane_off1), 0,
+                                                 0, 0);
     }
 }
 
@@ -255,15 +271,20 @@ __device__ __forceinline__ void row_sums(const f16x8 (&pop)[kQB][4], v4f (&l)[kQ
         for (int qb = 0; qb < kQB; ++qb) l[qb] = mfma16(ones, pop[qb][j], l[qb]);
 }
 
-// Everything one wave carries through the key loop.  Lane (r16, g) of a
-// 16x16 accumulator holds rows 4g..4g+3 of column r16; every score and
-// output block uses that layout (scores: rows = keys, columns = queries;
-// output: rows = head dims, columns = queries).  kDB_: live 16-dim output
-// blocks (o[db] for db >= kDB_ is never touched).
-template <int kDB_>
+// Everything one wave carries through the key loop, in the 16x16 layout
+// (head dims up to 96).  Lane (r16, g) of a 16x16 accumulator holds rows
+// 4g..4g+3 of column r16; every score and output block uses that layout
+// (scores: rows = keys, columns = queries; output: rows = head dims,
+// columns = queries).  kDC_: live 32-dim chunks of Q K^T; kDB_: live 16-dim
+// output blocks (o[db] for db >= kDB_ is never touched).
+template <int kDC_, int kDB_>
 struct Wave {
+    static constexpr int kDC = kDC_;
     static constexpr int kDB = kDB_;
     static constexpr bool kBlockRescale = true;   // rescale decisions per 16-query block
+    static constexpr bool kConvertInTail = false;  // code conversions after P V (see key_loop)
+    typedef v4f Scores[8][kQB];   // s[kb][qb]: keys 16kb + 4g + i of query r16
+    typedef f16x8 POps[kQB][4];   // P^T operands of one key tile (pack_f16)
     const uint8_t* k8;
     const uint8_t* v8;
     uint32_t row_stride;   // bytes between tokens of one head (uniform)
@@ -278,11 +299,52 @@ struct Wave {
     v4f o[8][kQB];         // O^T blocks [d block][query block]
     v4f l[kQB];            // running row sums of the fp16 p per query (the 4 entries are equal)
 
+    // Lane offsets (after wave and row_stride are set).  Async loads: lane
+    // covers row lane >> 3 of each 8-row segment, LDS chunk lane & 7, and
+    // fetches the logical chunk that the staging swizzle puts there:
+    // (lane & 7) ^ 4 (row & 1) for K; (lane & 7) ^ swz_v8(row) for V, where
+    // the tile row 16 wave + 8r + (lane >> 3) has bit 4 = wave & 1 for both of
+    // the wave's segments.
+    __device__ __forceinline__ void setup(int tid) {
+        const uint32_t lane = (uint32_t)tid & 63, r16 = lane & 15, g = lane >> 4;
+        k_rd = k_operand_offset((int)r16, (int)g);
+        vt_rd = r16 * kRow + 16 * (g ^ swz_vt(r16));
+        g_ld = (lane >> 3) * row_stride + 16 * ((lane & 7) ^ (4 * ((lane >> 3) & 1)));
+        g_ldv = (lane >> 3) * row_stride + 16 * ((lane & 7) ^ swz_v8((lane >> 3) + 16 * ((uint32_t)wave & 1)));
+        cv = (uint32_t)tid & (kGroupThreads - 1);
+        g4 = 4 * (int)g;
+    }
+    // Q operand (B of S = K Q^T, fp16 16x16x32): for the c-th MFMA, lane
+    // holds query r16 of the block and head dims 32c + 8g .. + 7, the
+    // mapping the K operand uses.
+    __device__ __forceinline__ void load_q(const uint8_t* __restrict__ q8, int q0, int lane) {
+        const int r16 = lane & 15, g = lane >> 4;
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) {
+            const int qi = q0 + wave * (16 * kQB) + qb * 16 + r16;
+#pragma unroll
+            for (int c = 0; c < kDC; ++c) {
+                u32x2 a = {0, 0};
+                if (qi < seq_hi) a = *(const u32x2*)(q8 + (size_t)qi * row_stride + (size_t)h * kD + 32 * c + 8 * g);
+                q[qb][c] = codes_to_f16x8(a[0], a[1]);
+            }
+        }
+    }
+    __device__ __forceinline__ void reset() {
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) {
+#pragma unroll
+            for (int db = 0; db < kDB; ++db) o[db][qb] = v4f{0, 0, 0, 0};
+            l[qb] = v4f{0, 0, 0, 0};
+            mc[qb] = kMInit;
+        }
+    }
+
     __device__ __forceinline__ void load_k8(lds_u8* lds, int t) const {
-        issue_code_tile_load(k8, row_stride, h, k0 + t * kBN, seq_hi, lds + kLdsK8, wave, g_ld);
+        issue_code_tile_load(k8, row_stride, h, k0 + t * kBN, seq_hi, lds + kLdsK8, wave, g_ld, g_ld);
     }
     __device__ __forceinline__ void load_v8(lds_u8* lds, int t) const {
-        issue_code_tile_load(v8, row_stride, h, k0 + t * kBN, seq_hi, lds + kLdsV8, wave, g_ldv);
+        issue_code_tile_load(v8, row_stride, h, k0 + t * kBN, seq_hi, lds + kLdsV8, wave, g_ldv, g_ldv);
     }
     __device__ __forceinline__ void convert_k(unsigned char* smem, int buf) const {
         convert_k_tile(smem + kLdsK8, smem + kLdsK + buf * kTileBytes, cv);
@@ -290,25 +352,378 @@ struct Wave {
     __device__ __forceinline__ void convert_v(unsigned char* smem, int buf) const {
         convert_vt(smem + kLdsV8, smem + kLdsV + buf * kTileBytes, cv);
     }
+
+    // The four phases of a key tile (see key_loop).
+    __device__ __forceinline__ void qk(const unsigned char* ktile, Scores& s) const { qk_tile<kDC>(ktile, k_rd, q, s); }
+    __device__ __forceinline__ void head(Scores& s, int nk) { softmax_head<kSplit>(*this, s, nk); }
+    __device__ __forceinline__ void tail(Scores& s, int nk, POps& pop) const {
+        exp_blocks<kSplit, 8>(*this, s, nk);
+        pack_f16(s, pop);
+    }
+    __device__ __forceinline__ void pv(const unsigned char* vttile, const POps& pop) {
+        pv_tile_t<kDB>(vttile, vt_rd, pop, o);
+        row_sums(pop, l);
+    }
+
+    // Epilogue: lane holds O^T[d = 16db + 4g + i][query r16]; the output rows
+    // hold head_dim dims (a multiple of 8, so a lane's 4 dims are all inside
+    // or all past it).  out = bf16(O * s_v / l).
+    __device__ __forceinline__ void store(__bf16* __restrict__ out, int q0, int num_heads, int head_dim, float s_v,
+                                          int lane) const {
+        const int r16 = lane & 15, g = lane >> 4;
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) {
+            const int qi = q0 + wave * (16 * kQB) + qb * 16 + r16;
+            if (qi < seq_hi) {
+                const float f = s_v / l[qb][0];
+                __bf16* dst = out + ((size_t)qi * num_heads + h) * head_dim + 4 * g;
+#pragma unroll
+                for (int db = 0; db < kDB; ++db) {
+                    if (16 * db + 4 * g < head_dim) {
+                        bf16x4 r;
+                        r[0] = (__bf16)(o[db][qb][0] * f);
+                        r[1] = (__bf16)(o[db][qb][1] * f);
+                        r[2] = (__bf16)(o[db][qb][2] * f);
+                        r[3] = (__bf16)(o[db][qb][3] * f);
+                        *(bf16x4*)(dst + 16 * db) = r;
+                    }
+                }
+            }
+        }
+    }
+    // Split-key partial: O / l in code units as fp16, and (mc, l).
+    __device__ __forceinline__ void store_partial(_Float16* __restrict__ part_o, v2f* __restrict__ part_ml,
+                                                  size_t prow0, int q0, int lane) const {
+        const int r16 = lane & 15, g = lane >> 4;
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) {
+            const int qt = wave * (16 * kQB) + qb * 16 + r16;   // query in tile
+            if (q0 + qt < seq_hi) {
+                const float il = 1.0f / l[qb][0];
+                _Float16* dst = part_o + (prow0 + qt) * kD + 4 * g;
+#pragma unroll
+                for (int db = 0; db < kDB; ++db) {
+                    f16x4 r;
+                    r[0] = (_Float16)(o[db][qb][0] * il);
+                    r[1] = (_Float16)(o[db][qb][1] * il);
+                    r[2] = (_Float16)(o[db][qb][2] * il);
+                    r[3] = (_Float16)(o[db][qb][3] * il);
+                    *(f16x4*)(dst + 16 * db) = r;
+                }
+                if (g == 0) part_ml[prow0 + qt] = v2f{mc[qb], l[qb][0]};
+            }
+        }
+    }
+};
+
+// ---- The 32x32 layout (head dims above 96) ----
+//
+// Both products run on v_mfma_f32_32x32x16_f16.  An operand read (1 KiB
+// per wave) then feeds one 32x32x16 product instead of two 16x16x32 ones:
+// the same LDS bytes per multiply-add, half the MFMA instructions and the
+// waits that go with them, which leaves more issue cycles to the wave that
+// runs the softmax on the same SIMD.  Lane l = (c32, hh), c32 = l & 31,
+// hh = l >> 5.
+//   Operands (A of both products, 16 B per lane): row c32 of a 32-row block,
+//     logical 16-byte chunk 2c + hh of the 16-element k-step c.  K and V^T
+//     tiles both place logical chunk j of row r at j ^ (r & 15), so one lane
+//     offset rd = c32 * kRow + 16 (hh ^ (c32 & 15)) serves both, at rd ^ 32c
+//     (+ 32 rows per block).
+//   Q (B of S = K Q^T): query c32 of the wave's 32, head dims 16c + 8hh + e.
+//   Accumulators: register r of 32x32 block b holds row
+//     32b + 8(r >> 2) + 4hh + (r & 3) of column c32.  In S the rows are
+//     keys, in O^T head dims, and the column is the lane's query: a lane
+//     holds 64 of its query's 128 scores of a tile, the lane l ^ 32 the
+//     rest.
+//   P^T (B of O^T += V^T P^T) for the 16-key step m: registers
+//     8(m & 1) .. 8(m & 1) + 7 of S block m >> 1, whose element e is key
+//     16m + 8(e >> 2) + 4hh + (e & 3).  The V^T tile holds the same keys in
+//     the same order in logical chunk 2m + hh of each row (convert_vt32).
+typedef float v16f __attribute__((ext_vector_type(16)));
+__device__ inline v16f mfma32(f16x8 a, f16x8 b, v16f c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// V code staging of the 32x32 layout, swizzled at 16-byte granularity like
+// swz_v8: a transposed read takes one 16-byte column chunk of the 8 rows
+// {16m + 4hh + 8a + i : a < 2, i < 4}, which differ in row bits 0, 1 and 3;
+// swz_v8w maps those to distinct chunks, and row bit 2 flips chunk bit 0.
+__device__ inline uint32_t swz_v8w(uint32_t k) { return ((k & 3) | ((k >> 1) & 4)) ^ ((k >> 2) & 1); }
+
+// Staged V codes -> one V^T tile of the 32x32 layout, by the 256 threads of
+// one wave group.  With the lane mapping of ds_read_b64_tr_b8 (convert_vt),
+// 16-lane group G of wave gw takes the 16-key step m = 2gw + (G >> 1) and
+// half hh = G & 1: source lane s points at key row
+// 16m + 4hh + 8(s >> 3) + ((s >> 1) & 3), low (s even) or high (s odd) 8
+// bytes of its 16-byte chunk n, so that lane r receives, for dim 16n + r,
+// key 16m + 8(e >> 2) + 4hh + (e & 3) at element e: logical chunk 2m + hh
+// of V^T row 16n + r, stored with one ds_write_b128.
+__device__ __forceinline__ void convert_vt32(const unsigned char* src, unsigned char* dst, uint32_t u) {
+    typedef int v2i __attribute__((ext_vector_type(2)));
+    const uint32_t grp = (u >> 4) & 3, r = u & 15;
+    const uint32_t m = 2 * (u >> 6) + (grp >> 1), hh = grp & 1;
+    const uint32_t krow = 16 * m + 4 * hh + 8 * (r >> 3) + ((r >> 1) & 3);
+    const uint32_t src_off = krow * kD + 16 * swz_v8w(krow) + 8 * (r & 1);
+    const uint32_t dst_off = r * kRow + 16 * ((2 * m + hh) ^ swz_vt(r));
+    v2i x[8];
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+        x[n] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) v2i*)(lds_u8*)(src + (src_off ^ (uint32_t)(n << 4))));
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+        *(f16x8*)(dst + dst_off + n * 16 * kRow) = codes_to_f16x8((uint32_t)x[n][0], (uint32_t)x[n][1]);
+}
+
+// S = K Q^T for one key tile: step n multiplies K operand (32-key block
+// n & 3, 16-dim step n >> 2) into S block n & 3, so products into one
+// accumulator are four steps apart.  Operands are requested kAhead steps
+// before their product issues.
+__device__ __forceinline__ void qk_tile32(const unsigned char* kbase, uint32_t rd, const f16x8 (&q)[8],
+                                          v16f (&s)[4]) {
+    constexpr int kSteps = 32;
+    constexpr int kAhead = 4;
+    auto operand = [&](int n) {
+        return *(const f16x8*)(kbase + (rd ^ (uint32_t)((n >> 2) << 5)) + (n & 3) * 32 * kRow);
+    };
+    f16x8 kop[8];
+#pragma unroll
+    for (int n = 0; n < kAhead; ++n) kop[n] = operand(n);
+#pragma unroll
+    for (int n = 0; n < kSteps; ++n) {
+        if (n + kAhead < kSteps) kop[(n + kAhead) & 7] = operand(n + kAhead);
+        __builtin_amdgcn_sched_barrier(0);
+        const int kb = n & 3, c = n >> 2;
+        s[kb] = mfma32(kop[n & 7], q[c], c == 0 ? v16f{} : s[kb]);
+    }
+}
+
+// l += the row sums of the fp16 p, on the 16x16x32 MFMA.  Fed as its B
+// operand, pop[m] of lane l = c + 16g (c < 16) lands in column c, k-group g;
+// lanes c and c + 32 (g = 0, 2) hold the 16 keys of query c, lanes c + 16 and
+// c + 48 (g = 1, 3) those of query c + 16.  The selector A (WaveWide::sel)
+// has ones in row 4g' (g' < 4) over the k-groups of parity g' & 1, so output
+// row 4g' of column c, which lane c + 16g' holds in entry 0, is the row sum
+// of that lane's own query; the other rows are zero.
+//
+// O^T += V^T P^T for one key tile: step n multiplies the V^T operand (32-dim
+// block n & 3, 16-key step n >> 2) with P^T of that key step.  The row sums
+// of each key step (above) are interleaved after its last product, so
+// that consecutive row-sum products, which share one accumulator, issue
+// five products apart.
+__device__ __forceinline__ void pv_tile32(const unsigned char* vtbase, uint32_t rd, const f16x8 (&pop)[8],
+                                          f16x8 sel, v16f (&o)[4], v4f& l) {
+    constexpr int kSteps = 32;
+    constexpr int kAhead = 3;
+    auto operand = [&](int n) {
+        return *(const f16x8*)(vtbase + (rd ^ (uint32_t)((n >> 2) << 5)) + (n & 3) * 32 * kRow);
+    };
+    f16x8 vop[4];
+#pragma unroll
+    for (int n = 0; n < kAhead; ++n) vop[n] = operand(n);
+#pragma unroll
+    for (int n = 0; n < kSteps; ++n) {
+        if (n + kAhead < kSteps) vop[(n + kAhead) & 3] = operand(n + kAhead);
+        __builtin_amdgcn_sched_barrier(0);
+        o[n & 3] = mfma32(vop[n & 3], pop[n >> 2], o[n & 3]);
+        if ((n & 3) == 3) l = mfma16(sel, pop[n >> 2], l);
+    }
+}
+
+// P^T operands from p, rounded to fp16 (nearest even): pop[m] = registers
+// 8(m & 1) .. + 7 of S block m >> 1.
+__device__ __forceinline__ void pack_f16_32(const v16f (&p)[4], f16x8 (&pop)[8]) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const v16f& a = p[m >> 1];
+        const int r = 8 * (m & 1);
+        pop[m] = f16x8{(_Float16)a[r], (_Float16)a[r + 1], (_Float16)a[r + 2], (_Float16)a[r + 3],
+                       (_Float16)a[r + 4], (_Float16)a[r + 5], (_Float16)a[r + 6], (_Float16)a[r + 7]};
+    }
+}
+
+struct WaveWide {
+    static constexpr int kDB = 4;   // 32-dim output blocks
+    static constexpr bool kConvertInTail = true;   // code conversions after the softmax tails (see key_loop)
+    typedef v16f Scores[4];         // s[kb]: 32-key block kb (layout above)
+    typedef f16x8 POps[8];          // P^T operands of the tile's 8 16-key steps
+    const uint8_t* k8;
+    const uint8_t* v8;
+    uint32_t row_stride;
+    int h, seq_hi, k0, nt, nk_last, wave;
+    float cexp;
+    uint32_t rd;                     // operand offset inside an fp16 K or V^T tile
+    uint32_t g_ld, g_ldv0, g_ldv1;   // async loads: K segments; V segments 0 and 1
+    uint32_t cv;
+    int hh4;                         // 4 hh: first key row of this lane inside an 8-key group
+    f16x8 sel;                       // A operand of the row-sum products (pv_tile32)
+    f16x8 q[8];                      // Q operand, one per 16-dim step
+    float mc;                        // running row max of the lane's query (log2 units)
+    v16f o[4];                       // O^T blocks of the lane's query
+    v4f l;                           // entry 0: row sum of the lane's query
+
+    // Lane offsets (after wave and row_stride are set).  Async V loads: the
+    // tile row 16 wave + 8r + (lane >> 3) of segment r has swz_v8w of its
+    // low four bits, 8r + (lane >> 3), so the two segments differ.
+    __device__ __forceinline__ void setup(int tid) {
+        const uint32_t lane = (uint32_t)tid & 63, c32 = lane & 31, hh = lane >> 5;
+        const uint32_t r16 = lane & 15, g = lane >> 4;
+        rd = c32 * kRow + 16 * (hh ^ (c32 & 15));
+        g_ld = (lane >> 3) * row_stride + 16 * ((lane & 7) ^ (4 * ((lane >> 3) & 1)));
+        g_ldv0 = (lane >> 3) * row_stride + 16 * ((lane & 7) ^ swz_v8w(lane >> 3));
+        g_ldv1 = (lane >> 3) * row_stride + 16 * ((lane & 7) ^ swz_v8w(8 + (lane >> 3)));
+        cv = (uint32_t)tid & (kGroupThreads - 1);
+        hh4 = 4 * (int)hh;
+        const _Float16 one = (_Float16)(((r16 & 3) == 0 && (g & 1) == ((r16 >> 2) & 1)) ? 1.0f : 0.0f);
+        sel = f16x8{one, one, one, one, one, one, one, one};
+    }
+    __device__ __forceinline__ void load_q(const uint8_t* __restrict__ q8, int q0, int lane) {
+        const int c32 = lane & 31, hh = lane >> 5;
+        const int qi = q0 + wave * 32 + c32;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            u32x2 a = {0, 0};
+            if (qi < seq_hi) a = *(const u32x2*)(q8 + (size_t)qi * row_stride + (size_t)h * kD + 16 * c + 8 * hh);
+            q[c] = codes_to_f16x8(a[0], a[1]);
+        }
+    }
+    __device__ __forceinline__ void reset() {
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) o[db] = v16f{};
+        l = v4f{0, 0, 0, 0};
+        mc = kMInit;
+    }
+
+    __device__ __forceinline__ void load_k8(lds_u8* lds, int t) const {
+        issue_code_tile_load(k8, row_stride, h, k0 + t * kBN, seq_hi, lds + kLdsK8, wave, g_ld, g_ld);
+    }
+    __device__ __forceinline__ void load_v8(lds_u8* lds, int t) const {
+        issue_code_tile_load(v8, row_stride, h, k0 + t * kBN, seq_hi, lds + kLdsV8, wave, g_ldv0, g_ldv1);
+    }
+    __device__ __forceinline__ void convert_k(unsigned char* smem, int buf) const {
+        convert_k_tile(smem + kLdsK8, smem + kLdsK + buf * kTileBytes, cv);
+    }
+    __device__ __forceinline__ void convert_v(unsigned char* smem, int buf) const {
+        convert_vt32(smem + kLdsV8, smem + kLdsV + buf * kTileBytes, cv);
+    }
+
+    // Keys past nk (the last tile) get `dead`: -inf before the max, 0 after
+    // the exponentials (also where c = 0 made -inf * c a NaN).
+    template <int kLo, int kHi>
+    __device__ __forceinline__ void mask(Scores& s, int nk, float dead) const {
+#pragma unroll
+        for (int kb = kLo; kb < kHi; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                s[kb][r] = hh4 >= nk - (32 * kb + 8 * (r >> 2) + (r & 3)) ? dead : s[kb][r];
+    }
+    template <int kLo, int kHi>
+    __device__ __forceinline__ void exponentials(Scores& s, int nk) const {
+        const float bias = 8.0f - mc;
+#pragma unroll
+        for (int kb = kLo; kb < kHi; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], cexp, bias));
+        if (nk < kBN) mask<kLo, kHi>(s, nk, 0.0f);
+    }
+
+    // The four phases of a key tile (see key_loop).  head: mask, the query's
+    // tile max tm (its 64 scores here, then the other half-wave's), and when
+    // tm outgrew mc by more than the slack for any query of the wave, mc
+    // moves to max(mc, tm + headroom) and O and l are rescaled; then p of S
+    // blocks 0 and 1.  tail: p of blocks 2 and 3, and the P^T operands.
+    __device__ __forceinline__ void qk(const unsigned char* ktile, Scores& s) const { qk_tile32(ktile, rd, q, s); }
+    __device__ __forceinline__ void head(Scores& s, int nk) {
+        if (nk < kBN) mask<0, 4>(s, nk, -INFINITY);
+        float mx = s[0][0];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        const v2i a = __builtin_amdgcn_permlane32_swap(__float_as_int(mx), __float_as_int(mx), false, false);
+        const float tm = fmaxf(__int_as_float(a[0]), __int_as_float(a[1])) * cexp;
+        if (__any(tm - mc > kRescaleSlack)) {
+            const float mnew = fmaxf(mc, tm + kRescaleHeadroom);
+            const float alpha = __builtin_amdgcn_exp2f(mc - mnew);
+            mc = mnew;
+            l *= alpha;
+#pragma unroll
+            for (int db = 0; db < kDB; ++db) o[db] *= alpha;
+        }
+        exponentials<0, 2>(s, nk);
+    }
+    __device__ __forceinline__ void tail(Scores& s, int nk, POps& pop) const {
+        exponentials<2, 4>(s, nk);
+        pack_f16_32(s, pop);
+    }
+    __device__ __forceinline__ void pv(const unsigned char* vttile, const POps& pop) {
+        pv_tile32(vttile, rd, pop, sel, o, l);
+    }
+
+    // Epilogue: register 4j + i of block db holds dim 32db + 8j + 4hh + i of
+    // the lane's query.
+    __device__ __forceinline__ void store(__bf16* __restrict__ out, int q0, int num_heads, int head_dim, float s_v,
+                                          int lane) const {
+        const int c32 = lane & 31, hh = lane >> 5;
+        const int qi = q0 + wave * 32 + c32;
+        if (qi >= seq_hi) return;
+        const float f = s_v / l[0];
+        __bf16* dst = out + ((size_t)qi * num_heads + h) * head_dim + 4 * hh;
+#pragma unroll
+        for (int db = 0; db < kDB; ++db)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (32 * db + 8 * j + 4 * hh < head_dim) {
+                    bf16x4 r;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) r[i] = (__bf16)(o[db][4 * j + i] * f);
+                    *(bf16x4*)(dst + 32 * db + 8 * j) = r;
+                }
+            }
+    }
+    __device__ __forceinline__ void store_partial(_Float16* __restrict__ part_o, v2f* __restrict__ part_ml,
+                                                  size_t prow0, int q0, int lane) const {
+        const int c32 = lane & 31, hh = lane >> 5;
+        const int qt = wave * 32 + c32;   // query in tile
+        if (q0 + qt >= seq_hi) return;
+        const float il = 1.0f / l[0];
+        _Float16* dst = part_o + (prow0 + qt) * kD + 4 * hh;
+#pragma unroll
+        for (int db = 0; db < kDB; ++db)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                f16x4 r;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) r[i] = (_Float16)(o[db][4 * j + i] * il);
+                *(f16x4*)(dst + 32 * db + 8 * j) = r;
+            }
+        if (hh == 0) part_ml[prow0 + qt] = v2f{mc, l[0]};
+    }
 };
 
 // The key loop of one wave group.  Period t (t = 0..nt) has four slots
 // separated by workgroup barriers (see the table at the top).  Loads: codes
 // of K_{t+1} into the K staging buffer at slot 1 (landing by the end of
-// slot 2, converted by A at slot 4), codes of V_{t+1} into the V staging
-// buffer at slot 3 (landing by the end of slot 4, converted by B at slot 2
-// of period t+1).  Buffer lifetimes: fp16 K_t is read in slots 1 (A) and 3
-// (B) of period t and rewritten with K_{t+2} at slot 4 of period t+1; fp16
-// V^T_t is written at slot 2 of period t, read in slot 4 of period t (A) and
-// slot 2 of period t+1 (B, which writes V^T_{t+1} into the other buffer in
-// the same slot), and rewritten with V^T_{t+2} at slot 2 of period t+2; each
-// staging buffer is converted before the next load into it is issued.
-template <bool kB, int kDC, int kDB>
-__device__ __forceinline__ void key_loop(Wave<kDB>& w, unsigned char* smem) {
+// slot 2), codes of V_{t+1} into the V staging buffer at slot 3 (landing by
+// the end of slot 4).  W is the wave's layout (Wave or WaveWide), which
+// supplies the phases and says where the code conversions go:
+//   after P V (W::kConvertInTail false): K_{t+1} by A at slot 4 of period t,
+//     V_{t+1} by B at slot 2 of period t+1, in the slot of the other group's
+//     softmax head;
+//   after the softmax tails (true): K_{t+1} by A at slot 3 of period t,
+//     V_{t+1} by B at slot 1 of period t+1, next to the other group's Q K^T.
+// Either way: fp16 K_t is read in slots 1 (A) and 3 (B) of period t and
+// rewritten with K_{t+2} in period t+1; fp16 V^T_t is written in slot 1 or 2
+// of period t, read in slot 4 of period t (A) and slot 2 of period t+1 (B),
+// and rewritten with V^T_{t+2} in period t+2 (the other buffer holds
+// V^T_{t+1}); each staging buffer is converted before the next load into it
+// is issued.
+template <bool kB, class W>
+__device__ __forceinline__ void key_loop(W& w, unsigned char* smem) {
     lds_u8* const lds = (lds_u8*)smem;
     const int nt = w.nt;
-    v4f s[8][kQB];
-    f16x8 pop[kQB][4];
+    typename W::Scores s;
+    typename W::POps pop;
     for (int t = 0; t <= nt; ++t) {
         const int cur = t & 1, prev = cur ^ 1;
         const int nk_t = (t + 1 < nt) ? kBN : w.nk_last;   // valid keys of tile t (t < nt)
@@ -318,26 +733,27 @@ __device__ __forceinline__ void key_loop(Wave<kDB>& w, unsigned char* smem) {
         if constexpr (!kB) {
             if (t < nt) {
                 mfma_phase_begin();
-                qk_tile<kDC>(smem + kLdsK + cur * kTileBytes, w.k_rd, w.q, s);
+                w.qk(smem + kLdsK + cur * kTileBytes, s);
                 mfma_phase_end();
             }
         } else {
-            if (t >= 1) {
-                exp_blocks<kSplit, 8>(w, s, nk_p);
-                pack_f16(s, pop);
+            if (t >= 1) w.tail(s, nk_p, pop);
+            if constexpr (W::kConvertInTail) {
+                if (t >= 1 && t < nt) w.convert_v(smem, cur);
             }
         }
         __syncthreads();
         // slot 2
         if constexpr (!kB) {
-            if (t < nt) softmax_head<kSplit>(w, s, nk_t);
+            if (t < nt) w.head(s, nk_t);
         } else {
             if (t >= 1) {
                 mfma_phase_begin();
-                pv_tile_t<kDB>(smem + kLdsV + prev * kTileBytes, w.vt_rd, pop, w.o);
-                row_sums(pop, w.l);
+                w.pv(smem + kLdsV + prev * kTileBytes, pop);
             }
-            if (t >= 1 && t < nt) w.convert_v(smem, cur);
+            if constexpr (!W::kConvertInTail) {
+                if (t >= 1 && t < nt) w.convert_v(smem, cur);
+            }
             mfma_phase_end();
         }
         wait_async_loads();
@@ -345,14 +761,14 @@ __device__ __forceinline__ void key_loop(Wave<kDB>& w, unsigned char* smem) {
         // slot 3
         if (t + 1 < nt) w.load_v8(lds, t + 1);
         if constexpr (!kB) {
-            if (t < nt) {
-                exp_blocks<kSplit, 8>(w, s, nk_t);
-                pack_f16(s, pop);
+            if (t < nt) w.tail(s, nk_t, pop);
+            if constexpr (W::kConvertInTail) {
+                if (t + 1 < nt) w.convert_k(smem, prev);
             }
         } else {
             if (t < nt) {
                 mfma_phase_begin();
-                qk_tile<kDC>(smem + kLdsK + cur * kTileBytes, w.k_rd, w.q, s);
+                w.qk(smem + kLdsK + cur * kTileBytes, s);
                 mfma_phase_end();
             }
         }
@@ -361,13 +777,14 @@ __device__ __forceinline__ void key_loop(Wave<kDB>& w, unsigned char* smem) {
         if constexpr (!kB) {
             if (t < nt) {
                 mfma_phase_begin();
-                pv_tile_t<kDB>(smem + kLdsV + cur * kTileBytes, w.vt_rd, pop, w.o);
-                row_sums(pop, w.l);
+                w.pv(smem + kLdsV + cur * kTileBytes, pop);
             }
-            if (t + 1 < nt) w.convert_k(smem, prev);
+            if constexpr (!W::kConvertInTail) {
+                if (t + 1 < nt) w.convert_k(smem, prev);
+            }
             mfma_phase_end();
         } else {
-            if (t < nt) softmax_head<kSplit>(w, s, nk_t);
+            if (t < nt) w.head(s, nk_t);
         }
         wait_async_loads();
         __syncthreads();
@@ -382,7 +799,7 @@ __device__ __forceinline__ void key_loop(Wave<kDB>& w, unsigned char* smem) {
 // running max in log2 units and its row sum.  attn_combine_kernel merges the
 // ranges.  Partial rows are indexed [split][head][virtual tile][query in
 // tile] and hold 128 fp16 dims (those past the live blocks unwritten).
-template <int kDC, int kDB, bool kPartial>
+template <class W, bool kPartial>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8, const uint8_t* __restrict__ v8,
     const float* __restrict__ scales, const int32_t* __restrict__ cu, int num_seqs, int num_heads,
@@ -392,7 +809,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     lds_u8* const lds = (lds_u8*)smem;
 
     const int tid = threadIdx.x, lane = tid & 63;
-    const int r16 = lane & 15, g = lane >> 4;
 
     // logical id = (head, key range, virtual query tile): consecutive ids
     // share one head's K/V range and land on one XCD
@@ -420,7 +836,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
         }
     }
 
-    Wave<kDB> w;
+    W w;
     w.k8 = k8;
     w.v8 = v8;
     w.row_stride = (uint32_t)num_heads * kD;
@@ -431,46 +847,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     w.nk_last = min(kBN, seq_hi - (w.k0 + (nt - 1) * kBN));
     w.wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in an SGPR
     const bool group_b = w.wave >= kWaves / 2;          // wave-uniform
-    w.k_rd = k_operand_offset(r16, g);
-    w.vt_rd = (uint32_t)(r16 * kRow + 16 * ((uint32_t)g ^ swz_vt((uint32_t)r16)));
-    // Async loads: lane covers row lane >> 3 of each 8-row segment, LDS chunk
-    // lane & 7, and fetches the logical chunk that the staging swizzle puts
-    // there: (lane & 7) ^ 4 (row & 1) for K; (lane & 7) ^ swz_v8(row) for V,
-    // where the tile row 16 wave + 8r + (lane >> 3) has bit 4 = wave & 1 for
-    // both of the wave's segments.
-    w.g_ld = ((uint32_t)lane >> 3) * w.row_stride + 16 * (((uint32_t)lane & 7) ^ (4 * (((uint32_t)lane >> 3) & 1)));
-    w.g_ldv = ((uint32_t)lane >> 3) * w.row_stride +
-              16 * (((uint32_t)lane & 7) ^ swz_v8(((uint32_t)lane >> 3) + 16 * ((uint32_t)w.wave & 1)));
-    w.cv = (uint32_t)tid & (kGroupThreads - 1);
-    w.g4 = 4 * g;
+    w.setup(tid);
 
     // ---- prologue: codes of K_0 and V_0 in flight; Q operand; K_0 and V_0
     // converted (A: K, B: V) ----
     w.load_k8(lds, 0);
     w.load_v8(lds, 0);
-
-    // Q operand (B of S = K Q^T, fp16 16x16x32): for the c-th MFMA, lane
-    // holds query r16 of the block and head dims 32c + 8g .. + 7, the
-    // mapping the K operand uses.
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-        const int qi = q0 + w.wave * (16 * kQB) + qb * 16 + r16;
-#pragma unroll
-        for (int c = 0; c < kDC; ++c) {
-            u32x2 a = {0, 0};
-            if (qi < seq_hi) a = *(const u32x2*)(q8 + (size_t)qi * w.row_stride + (size_t)h * kD + 32 * c + 8 * g);
-            w.q[qb][c] = codes_to_f16x8(a[0], a[1]);
-        }
-    }
+    w.load_q(q8, q0, lane);
     const float s_q = scales[0], s_k = scales[1], s_v = scales[2];
     w.cexp = s_q * s_k * log2e_rsqrt_d;
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-#pragma unroll
-        for (int db = 0; db < kDB; ++db) w.o[db][qb] = v4f{0, 0, 0, 0};
-        w.l[qb] = v4f{0, 0, 0, 0};
-        w.mc[qb] = kMInit;
-    }
+    w.reset();
 
     wait_async_loads();
     __syncthreads();
@@ -485,53 +871,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     // loop, so its registers are allocated for its own live ranges; both
     // copies execute the same sequence of barriers.
     if (group_b)
-        key_loop<true, kDC, kDB>(w, smem);
+        key_loop<true>(w, smem);
     else
-        key_loop<false, kDC, kDB>(w, smem);
+        key_loop<false>(w, smem);
 
-    // ---- epilogue: lane holds O^T[d = 16db + 4g + i][query r16]; the output
-    // rows hold head_dim dims (a multiple of 8, so a lane's 4 dims are all
-    // inside or all past it) ----
-    if constexpr (kPartial) {
-#pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) {
-            const int qt = w.wave * (16 * kQB) + qb * 16 + r16;   // query in tile
-            if (q0 + qt < seq_hi) {
-                const float il = 1.0f / w.l[qb][0];
-                _Float16* dst = part_o + (prow0 + qt) * kD + 4 * g;
-#pragma unroll
-                for (int db = 0; db < kDB; ++db) {
-                    f16x4 r;
-                    r[0] = (_Float16)(w.o[db][qb][0] * il);
-                    r[1] = (_Float16)(w.o[db][qb][1] * il);
-                    r[2] = (_Float16)(w.o[db][qb][2] * il);
-                    r[3] = (_Float16)(w.o[db][qb][3] * il);
-                    *(f16x4*)(dst + 16 * db) = r;
-                }
-                if (g == 0) part_ml[prow0 + qt] = v2f{w.mc[qb], w.l[qb][0]};
-            }
-        }
-        return;
-    }
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-        const int qi = q0 + w.wave * (16 * kQB) + qb * 16 + r16;
-        if (qi < seq_hi) {
-            const float f = s_v / w.l[qb][0];
-            __bf16* dst = out + ((size_t)qi * num_heads + h) * head_dim + 4 * g;
-#pragma unroll
-            for (int db = 0; db < kDB; ++db) {
-                if (16 * db + 4 * g < head_dim) {
-                    bf16x4 r;
-                    r[0] = (__bf16)(w.o[db][qb][0] * f);
-                    r[1] = (__bf16)(w.o[db][qb][1] * f);
-                    r[2] = (__bf16)(w.o[db][qb][2] * f);
-                    r[3] = (__bf16)(w.o[db][qb][3] * f);
-                    *(bf16x4*)(dst + 16 * db) = r;
-                }
-            }
-        }
-    }
+    if constexpr (kPartial)
+        w.store_partial(part_o, part_ml, prow0, q0, lane);
+    else
+        w.store(out, q0, num_heads, head_dim, s_v, lane);
 }
 
 // Merge the key ranges of attn_fwd_kernel<.., true>.  Workgroup = 16
@@ -586,14 +933,36 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const _Float16* __res
     *(bf16x8*)(out + ((size_t)(q0 + qt) * num_heads + h) * head_dim + 8 * c) = r;
 }
 
-// The smallest instantiation whose 32-dim chunks and 16-dim blocks cover head_dim.
+// Largest launch (in workgroups) that runs the 32x32 layout on the current
+// device: 3/4 of its CUs, which leaves the board below its power limit (see
+// the top of the file); 0 if the device cannot be queried.
+long long wide_layout_max_workgroups() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cached[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    int v = cached[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 0;
+        v = 3 * cus / 4;
+        cached[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+// The kernel for a launch of `workgroups` at head_dim: above 96 dims the
+// 32x32 layout for launches below the power limit, else the 16x16 one; the
+// 16x16 instantiation is the smallest whose 32-dim chunks and 16-dim blocks
+// cover head_dim.
 template <bool kPartial>
-auto* attention_kernel_for(int head_dim) {
-    auto* kernel = attn_fwd_kernel<4, 8, kPartial>;
-    if (head_dim <= 32) kernel = attn_fwd_kernel<1, 2, kPartial>;
-    else if (head_dim <= 64) kernel = attn_fwd_kernel<2, 4, kPartial>;
-    else if (head_dim <= 80) kernel = attn_fwd_kernel<3, 5, kPartial>;
-    else if (head_dim <= 96) kernel = attn_fwd_kernel<3, 6, kPartial>;
+auto* attention_kernel_for(int head_dim, long long workgroups) {
+    auto* kernel = workgroups <= wide_layout_max_workgroups() ? attn_fwd_kernel<WaveWide, kPartial>
+                                                              : attn_fwd_kernel<Wave<4, 8>, kPartial>;
+    if (head_dim <= 32) kernel = attn_fwd_kernel<Wave<1, 2>, kPartial>;
+    else if (head_dim <= 64) kernel = attn_fwd_kernel<Wave<2, 4>, kPartial>;
+    else if (head_dim <= 80) kernel = attn_fwd_kernel<Wave<3, 5>, kPartial>;
+    else if (head_dim <= 96) kernel = attn_fwd_kernel<Wave<3, 6>, kPartial>;
     return kernel;
 }
 
@@ -657,14 +1026,14 @@ hipError_t launch_attention_split(const uint8_t* q8, const uint8_t* k8, const ui
     if (nwg * num_splits > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
     const float c = softmax_log2_factor(head_dim);
     if (num_splits <= 1) {
-        attention_kernel_for<false>(head_dim)<<<(unsigned)nwg, kThreads, 0, s>>>(
+        attention_kernel_for<false>(head_dim, nwg)<<<(unsigned)nwg, kThreads, 0, s>>>(
             q8, k8, v8, scales, cu_seqlens, num_seqs, num_heads, tph, 1, head_dim, c, (__bf16*)out, nullptr, nullptr);
         return hipGetLastError();
     }
     const size_t rows = (size_t)num_splits * nwg * kBM;
     _Float16* part_o = (_Float16*)workspace;
     v2f* part_ml = (v2f*)((char*)workspace + ((rows * kD * sizeof(_Float16) + 255) & ~(size_t)255));
-    attention_kernel_for<true>(head_dim)<<<(unsigned)(nwg * num_splits), kThreads, 0, s>>>(
+    attention_kernel_for<true>(head_dim, nwg * num_splits)<<<(unsigned)(nwg * num_splits), kThreads, 0, s>>>(
         q8, k8, v8, scales, cu_seqlens, num_seqs, num_heads, tph, num_splits, head_dim, c, nullptr, part_o, part_ml);
     attn_combine_kernel<<<(unsigned)(nwg * (kBM / kCombineQueries)), 256, 0, s>>>(
         part_o, part_ml, scales, cu_seqlens, num_seqs, num_heads, tph, num_splits, head_dim, (__bf16*)out);

@@ -204,7 +204,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_fwd_kernel(
         }
         w.g4 = 4 * g;
     }
-    const int nt = w.nt;
 
     // ---- prologue: K_0 and V_0 in flight; Q operand ----
     w.load_k(lds, 0, 0);

@@ -222,9 +222,10 @@ __device__ inline uint32_t v_operand_offset(int r16, int g) {
 // phase (Q K^T or P V) while the other runs exponentials, packing or code
 // conversion.  Without a hint the SIMD favours the older wave,
 // so group B's MFMA phases drew out behind A's vector work; raising the
-// priority of whichever wave is in an MFMA slot (the product and the code
-// conversion that follows it in the same slot) keeps the matrix pipe fed and
-// leaves the vector work to fill its gaps.
+// priority of whichever wave is in an MFMA slot (the product, and in the
+// E4M3 kernel's 16x16 layout the code conversion that follows it in the same
+// slot) keeps the matrix pipe fed and leaves the vector work to fill its
+// gaps.
 __device__ __forceinline__ void mfma_phase_begin() { __builtin_amdgcn_s_setprio(1); }
 __device__ __forceinline__ void mfma_phase_end() { __builtin_amdgcn_s_setprio(0); }
 
