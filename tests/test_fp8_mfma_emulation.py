@@ -10,8 +10,10 @@ in float64 (pinned to the probe's observed values), computes attention with
 it on the workloads' own codes, and compares with the exact logits, under the
 contract's measure e = |g - r| / max(1, |r|):
 
-* the 2304-token image (workload 2: N(0, sigma_h) Q and K, no outliers) stays
-  far inside the contract, even on the query rows with the largest codes;
+* the two outlier-free workloads stay far inside the contract, even on the
+  query rows with the largest codes: the 2304-token image (workload 2,
+  N(0, sigma_h) Q and K, static scales) and one 14400-token image of the QHD
+  batch (workload 4, the same distribution, dynamic scales);
 * the kernel-benchmark workload (workload 3: x20 outliers in 0.1 % of Q and K
   elements) breaks it on the rows that hold outliers: a product of two
   outliers truncates its 7 group-mates and moves the row's dominant logits.
@@ -52,22 +54,30 @@ def test_emulation_matches_the_probe():
         assert float((qa * kb).sum() + c00) == exact, name
 
 
-def _codes(widx, mode):
+def _codes(widx, mode, num_tokens=None):
     w = WORKLOADS[widx]
     if mode == "static":
-        sa = [oracle.amax(t.float().numpy()) for t in make_qkv(w, 0, calibration=True)]
+        sa = [oracle.amax(t.float().numpy()) for t in make_qkv(w, 0, calibration=True, num_tokens=num_tokens)]
         st = oracle.ScaleState(static_amax=sa, margin=1.5)
     else:
         st = oracle.ScaleState()
-    q8, k8, v8, descale, _ = oracle.quantize_qkv(st, mode, *(t.float().numpy() for t in make_qkv(w, 0)))
+    x = (t.float().numpy() for t in make_qkv(w, 0, num_tokens=num_tokens))
+    q8, k8, v8, descale, _ = oracle.quantize_qkv(st, mode, *x)
     return w, q8, k8, v8, descale
 
 
-def _worst_error(widx, mode, heads, rows_per_head):
+def _fp8_mfma_logits_chunked(q, k, keys=1024):
+    return np.concatenate([fp8_mfma_logits(q, k[j:j + keys]) for j in range(0, k.shape[0], keys)], axis=1)
+
+
+def _worst_error(widx, mode, heads, rows_per_head, num_tokens=None):
     """Max contract error over the given heads' rows_per_head query rows with
-    the largest |code| (the rows holding outliers), first sequence."""
-    w, q8, k8, v8, (s_q, s_k, s_v) = _codes(widx, mode)
+    the largest |code| (the rows holding outliers), first sequence.  With
+    num_tokens, the tokens drawn are only that many (the first sequence's
+    length), and the codes and scales come from them alone."""
+    w, q8, k8, v8, (s_q, s_k, s_v) = _codes(widx, mode, num_tokens)
     lo, hi = w.cu_seqlens[0], w.cu_seqlens[1]
+    assert hi <= q8.shape[0]
     c = float(s_q) * float(s_k) / np.sqrt(128.0)
     worst = 0.0
     for h in heads:
@@ -84,9 +94,9 @@ def _worst_error(widx, mode, heads, rows_per_head):
         r = attend(q[rows] @ k.T)
         if h == heads[0]:   # the exact side is the oracle's attention on the same codes
             ref = oracle.attention_rows(q8[:, h:h + 1], k8[:, h:h + 1], v8[:, h:h + 1], (s_q, s_k, s_v),
-                                        np.array(w.cu_seqlens), lo + rows)
+                                        np.array([lo, hi]), lo + rows)
             assert np.allclose(r, ref[:, 0], rtol=1e-12, atol=1e-12)
-        g = attend(fp8_mfma_logits(q[rows], k))
+        g = attend(_fp8_mfma_logits_chunked(q[rows], k))
         worst = max(worst, float((np.abs(g - r) / np.maximum(1.0, np.abs(r))).max()))
     print(f"workload {widx} ({mode}): fp8-MFMA Q K^T, max e {worst:.3e}", flush=True)
     return worst
@@ -94,6 +104,12 @@ def _worst_error(widx, mode, heads, rows_per_head):
 
 def test_outlier_free_image_stays_inside_the_contract():
     assert _worst_error(2, "static", range(16), 64) < 0.1 * TOL_MAX
+
+
+@pytest.mark.timeout(300)
+def test_outlier_free_qhd_image_stays_inside_the_contract():
+    # one 14400-token image of the QHD batch: per-head sigma Q and K, unit V
+    assert _worst_error(4, "dynamic", (0, 5, 11, 15), 32, num_tokens=WORKLOADS[4].seqlens[0]) < 0.1 * TOL_MAX
 
 
 @pytest.mark.timeout(300)
