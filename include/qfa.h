@@ -189,6 +189,26 @@ qfa_status qfa_fp8_varlen_attn(const uint8_t* q8, const uint8_t* k8, const uint8
                                void* stream);
 
 /*
+ * The same attention with S = Q K^T on the fp8 matrix cores, like the
+ * per-tensor FP8 attention kernel that [P4] Requirements names for
+ * gfx942/gfx950, for inputs known to hold no isolated large elements.
+ * Arguments, layouts, limits and errors as qfa_fp8_varlen_attn.  For
+ * head_dim above 64, S is taken by v_mfma_f32_16x16x128_f8f6f4 on the codes
+ * themselves: no conversion of K and half the matrix cycles of S.  That
+ * instruction truncates every product in a group of 8 consecutive dims to a
+ * multiple of 2^(E - 13), E the exponent of the group's largest product, so
+ * a product of two outliers (say 20x the typical magnitude) wipes out the
+ * low bits of its 7 neighbours: the result can then miss the tolerance
+ * qfa_fp8_varlen_attn holds.  On Gaussian Q and K without outliers it stays
+ * as accurate as qfa_fp8_varlen_attn.  For head_dim <= 64 it runs
+ * qfa_fp8_varlen_attn's kernel (exact products).
+ */
+qfa_status qfa_fp8_varlen_attn_fp8qk(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                                     const float* scales, const int32_t* cu_seqlens, int num_seqs,
+                                     int64_t total_tokens, int num_heads, int head_dim, void* out,
+                                     void* stream);
+
+/*
  * The same attention with the keys of each (head, 256-query tile) split into
  * up to QFA_MAX_SPLITS ranges of whole 128-key tiles, one workgroup per
  * range, for launches that would leave compute units idle (small images:

@@ -344,6 +344,24 @@ qfa_status qfa_fp8_varlen_attn(const uint8_t* q8, const uint8_t* k8, const uint8
     return check_launch(e, where);
 }
 
+qfa_status qfa_fp8_varlen_attn_fp8qk(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* scales,
+                                     const int32_t* cu_seqlens, int num_seqs, int64_t total_tokens, int num_heads,
+                                     int head_dim, void* out, void* stream) {
+    const char* where = "qfa_fp8_varlen_attn_fp8qk";
+    int64_t n = 0;
+    qfa_status s = check_fp8_attn(q8, k8, v8, scales, cu_seqlens, num_seqs, total_tokens, num_heads, head_dim, out,
+                                  &n, where);
+    if (s != QFA_OK) return s;
+    s = check_attn_grid(num_seqs, total_tokens, num_heads, 1, where);
+    if (s != QFA_OK) return s;
+    s = check_pending(where);
+    if (s != QFA_OK) return s;
+    if (n == 0) return ok();
+    const hipError_t e = qfa::launch_attention_fp8qk(q8, k8, v8, scales, cu_seqlens, num_seqs, (int)total_tokens,
+                                                     num_heads, head_dim, out, (hipStream_t)stream);
+    return check_launch(e, where);
+}
+
 qfa_status qfa_bf16_varlen_attn(const void* q, const void* k, const void* v, const int32_t* cu_seqlens, int num_seqs,
                                 int64_t total_tokens, int num_heads, int head_dim, void* out, void* stream) {
     const char* where = "qfa_bf16_varlen_attn";

@@ -43,6 +43,11 @@ hipError_t launch_quantize_packed(DeviceState* st, bool dynamic, const uint16_t*
 hipError_t launch_attention(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* scales,
                             const int32_t* cu_seqlens, int num_seqs, int total_tokens, int num_heads, int head_dim,
                             void* out, hipStream_t s);
+// The same with S = K Q^T on the fp8 MFMA for head dims above 64 (the
+// exact kernel up to 64).
+hipError_t launch_attention_fp8qk(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* scales,
+                                  const int32_t* cu_seqlens, int num_seqs, int total_tokens, int num_heads,
+                                  int head_dim, void* out, hipStream_t s);
 // Split-key variant: num_splits key ranges per (head, query tile), partial
 // results in `workspace` (attention_workspace_bytes), merged by a second
 // kernel; num_splits <= 1 is launch_attention.

@@ -49,6 +49,9 @@ int main(void) {
            qfa_fp8_varlen_attn(dev, dev, dev, (const float*)dev, cu, 1, 4, 65537, 128, dev, NULL), QFA_ERR_SHAPE);
     expect("attention: misaligned output",
            qfa_fp8_varlen_attn(dev, dev, dev, (const float*)dev, cu, 1, 4, 1, 128, misaligned, NULL), QFA_ERR_ALIGN);
+    expect("fp8 QK^T attention: head_dim 130",
+           qfa_fp8_varlen_attn_fp8qk(dev, dev, dev, (const float*)dev, cu, 1, 4, 1, 130, dev, NULL),
+           QFA_ERR_UNSUPPORTED);
     expect("bf16 attention: head_dim 64",
            qfa_bf16_varlen_attn(dev, dev, dev, cu, 1, 4, 1, 64, dev, NULL), QFA_ERR_UNSUPPORTED);
     expect("export: null output", qfa_export_static_amax(&st, 1.5f, NULL, NULL), QFA_ERR_NULL);

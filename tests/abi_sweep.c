@@ -145,12 +145,15 @@ static void sweep_once(void) {
                                                              any_int(), any_int(), (uint8_t*)o, (uint8_t*)any_ptr(),
                                                              (uint8_t*)any_ptr(), NULL));
             break;
-        case 3:
-            check("attention", qfa_fp8_varlen_attn((const uint8_t*)q, (const uint8_t*)any_ptr(),
-                                                   (const uint8_t*)any_ptr(), (const float*)any_ptr(),
-                                                   (const int32_t*)any_ptr(), any_int(), any_i64(), any_int(),
-                                                   any_int(), o, NULL));
+        case 3: {
+            /* the exact attention and the fp8 Q K^T one share their arguments */
+            const int fp8qk = (int)pick(2);
+            const qfa_status r = (fp8qk ? qfa_fp8_varlen_attn_fp8qk : qfa_fp8_varlen_attn)(
+                (const uint8_t*)q, (const uint8_t*)any_ptr(), (const uint8_t*)any_ptr(), (const float*)any_ptr(),
+                (const int32_t*)any_ptr(), any_int(), any_i64(), any_int(), any_int(), o, NULL);
+            check(fp8qk ? "fp8 Q K^T attention" : "attention", r);
             break;
+        }
         case 4:
             check("split attention",
                   qfa_fp8_varlen_attn_split((const uint8_t*)q, (const uint8_t*)any_ptr(), (const uint8_t*)any_ptr(),
@@ -235,6 +238,8 @@ static void edges(void) {
                 const int nseq = kInts[i], heads = kInts[k];
                 const int64_t tokens = kI64[j];
                 check("edge attention", qfa_fp8_varlen_attn(c8, c8, c8, sc, cu, nseq, tokens, heads, 128, dev, NULL));
+                check("edge fp8 Q K^T attention",
+                      qfa_fp8_varlen_attn_fp8qk(c8, c8, c8, sc, cu, nseq, tokens, heads, 96, dev, NULL));
                 check("edge split", qfa_fp8_varlen_attn_split(c8, c8, c8, sc, cu, nseq, tokens, heads, 80, 0, dev,
                                                               SIZE_MAX, dev, NULL));
                 check("edge split, no allocation",

@@ -31,7 +31,7 @@ def header_functions():
 
 def test_header_symbols_exported():
     declared = header_functions()
-    assert len(declared) == 16, declared
+    assert len(declared) == 17, declared
     out = subprocess.run(["nm", "-D", "--defined-only", qfa.library_path()], stdout=subprocess.PIPE, text=True).stdout
     exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
     missing = [f for f in declared if f not in exported]
@@ -102,11 +102,13 @@ def test_quantize_validation():
     assert _quant(ctypes.byref(hs), mode=1, D=100) == UNSUP
 
 
-def _attn(q8=FAKE, k8=FAKE, v8=FAKE, sc=FAKE, cu=FAKE, B=1, T=8, H=2, D=128, out=FAKE):
-    return lib.qfa_fp8_varlen_attn(q8, k8, v8, sc, cu, B, T, H, D, out, None)
+@pytest.mark.parametrize("entry", ["qfa_fp8_varlen_attn", "qfa_fp8_varlen_attn_fp8qk"])
+def test_attention_validation(entry):
+    fn = getattr(lib, entry)
 
+    def _attn(q8=FAKE, k8=FAKE, v8=FAKE, sc=FAKE, cu=FAKE, B=1, T=8, H=2, D=128, out=FAKE):
+        return fn(q8, k8, v8, sc, cu, B, T, H, D, out, None)
 
-def test_attention_validation():
     for d in (0, 4, 100, 136, 256):
         assert _attn(D=d) == UNSUP, d
     assert _attn(H=0) == SHAPE

@@ -1,7 +1,9 @@
-"""What the fp8 MFMAs' summation would do to the workloads' attention (CPU).
+"""What the fp8 MFMAs' summation does to the workloads' attention (CPU).
 
-The E4M3 attention kernel runs Q K^T on the fp16 MFMA over exactly converted
-codes, at half the fp8 rate, instead of on v_mfma_f32_16x16x128_f8f6f4.
+The exact E4M3 attention kernel runs Q K^T on the fp16 MFMA over exactly
+converted codes, at half the fp8 rate; qfa_fp8_varlen_attn_fp8qk runs it on
+v_mfma_f32_16x16x128_f8f6f4 for inputs without outliers
+(tests/test_gpu_fp8qk.py checks it on the GPU).
 tests/test_gpu_mfma_hw.py pins how gfx950's fp8 MFMAs sum: within each group
 of 8 consecutive products, every product is cut toward zero to a multiple of
 2^(E - 13), E the exponent of the group's largest product; the groups and
@@ -18,9 +20,10 @@ contract's measure e = |g - r| / max(1, |r|):
   elements) breaks it on the rows that hold outliers: a product of two
   outliers truncates its 7 group-mates and moves the row's dominant logits.
 
-So fp8 Q K^T would be exact enough only for inputs known to be free of
-outliers, which the per-tensor scales cannot tell apart, and not for the
-workload the library is measured on.
+So fp8 Q K^T is exact enough only for inputs known to be free of outliers,
+which the per-tensor scales cannot tell apart, and not for the workload the
+library is measured on: that is the domain of the fp8 entry point, and the
+default path stays on the fp16 MFMA.
 """
 
 import numpy as np
