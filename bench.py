@@ -57,7 +57,8 @@ def parse():
                         "path on the small workloads (1x256 tokens x 2 heads, 1x2304 tokens x 16 heads)")
     p.add_argument("--all-configs", action="store_true",
                    help="instead of the benchmark, time every workload (quantize in its own mode, FP8 attention, the "
-                        "BF16 baseline); one JSON line per workload")
+                        "BF16 baseline, and Q K^T on the fp8 MFMA where Q and K carry no outliers); one JSON line per "
+                        "workload")
     p.add_argument("--seq-sweep", action="store_true",
                    help="instead of the benchmark, time single images of 2304, 4096, 8192 and 16384 tokens x 16 heads "
                         "(the kernel-benchmark recipe): FP8 step incl. quantize on the path the library picks, and "
@@ -67,10 +68,13 @@ def parse():
                         "(1 x 2304 tokens x 8 heads, 1 x 4608 x 4, 1 x 9216 x 2, 1 x 2304 x 16) for 1, 2, 3 and 6 key "
                         "ranges and the automatic count")
     p.add_argument("--power", action="store_true",
-                   help="instead of the benchmark, run the FP8 attention, the FP8 step, the BF16 baseline and a "
-                        "full-chip MFMA throughput kernel (f16, bf16, fp8) back to back for --power-s seconds each, "
-                        "reading socket power and GFX clocks with amd-smi meanwhile; one JSON line per item")
+                   help="instead of the benchmark, run the FP8 attention, the FP8 step, the BF16 baseline, the fp8 "
+                        "Q K^T attention and the exact one on outlier-free codes, and a full-chip MFMA throughput "
+                        "kernel (f16, bf16, fp8) back to back for --power-s seconds each, reading socket power and GFX "
+                        "clocks with amd-smi meanwhile; one JSON line per item")
     p.add_argument("--power-s", type=float, default=4.0)
+    p.add_argument("--no-fp8qk", action="store_true",
+                   help="skip the fp8_qk_outlier_free block (Q K^T on the fp8 MFMA, outlier-free inputs)")
     p.add_argument("--no-power-limited", action="store_true",
                    help="skip the 2 s sustained attention and matrix-throughput runs of the power_limited block")
     p.add_argument("--packed-head-dim", type=int, default=0,
@@ -162,6 +166,13 @@ def all_configs(steps, warmup, prewarm_s):
             split = {"num_splits": splits, "ms": round(ms_s, 4), "tflops": round(w.attn_flop / (ms_s * 1e-3) / 1e12, 1),
                      "step_incl_quant_ms": round(ms_q + ms_s, 4),
                      "fp8_speedup_incl_quant": round(ms_b / (ms_q + ms_s), 3)}
+        # Q K^T on the fp8 MFMA, for the workloads whose Q and K carry no outliers (the entry point's domain)
+        fp8qk = None
+        if w.outlier_p == 0.0:
+            ms_f = timed(lambda i: qfa.fp8_varlen_attn_fp8qk(*codes[i % n_sets], scs[i % n_sets], cu, H, out=out), n)
+            fp8qk = {"ms": round(ms_f, 4), "tflops": round(w.attn_flop / (ms_f * 1e-3) / 1e12, 1),
+                     "speedup_vs_exact": round(ms_a / ms_f, 3), "step_incl_quant_ms": round(ms_q + ms_f, 4),
+                     "fp8_speedup_incl_quant": round(ms_b / (ms_q + ms_f), 3)}
         qbytes = 3 * 3 * T * H * 128   # read 2 B and write 1 B per element (one pass)
         flop = w.attn_flop
         print(json.dumps({"config": {
@@ -175,6 +186,7 @@ def all_configs(steps, warmup, prewarm_s):
             "bf16_attention": {"ms": round(ms_b, 4), "tflops": round(flop / (ms_b * 1e-3) / 1e12, 1)},
             "fp8_speedup_incl_quant": round(ms_b / (ms_q + ms_a), 3),
             "fp8_split_attention": split,
+            "fp8_qk_attention": fp8qk,
             "launches": n}}), flush=True)
         del sets, codes, out
         torch.cuda.empty_cache()
@@ -477,6 +489,51 @@ CONTEXT = {
 }
 
 
+def fp8qk_outlier_free(w, qfa, torch, cu, out, stream, steps, workload_codes):
+    """fp8_varlen_attn_fp8qk (Q K^T on the fp8 MFMA) on the workload's shape and per-head sigmas without its
+    outliers -- the entry point's domain -- timed against the exact kernel on the same codes.  Its output is compared
+    elementwise with the exact kernel's (e = |a - b| / max(1, |b|)) there, and on the workload's own codes
+    (``workload_codes``: q8, k8, v8, scales), whose outliers put them outside that domain."""
+    import dataclasses
+
+    from workloads import make_qkv
+
+    wc = dataclasses.replace(w, outlier_p=0.0, outlier_scale=1.0)
+    q, k, v = make_qkv(wc, 0, device=out.device)
+    st = qfa.init_scale_state(out.device)
+    q8, k8, v8 = qfa.quantize_qkv(st, "dynamic", q, k, v)
+    del q, k, v
+    sc = qfa.descale(st)
+    H = w.num_heads
+    exact = qfa.fp8_varlen_attn(q8, k8, v8, sc, cu, H).float()
+    fast = qfa.fp8_varlen_attn_fp8qk(q8, k8, v8, sc, cu, H, out=out).float()
+    e = ((fast - exact).abs() / exact.abs().clamp(min=1.0)).max().item()
+
+    def loop(fn):
+        prewarm(fn, 0.05)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(steps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms_fast = loop(lambda i: qfa.fp8_varlen_attn_fp8qk(q8, k8, v8, sc, cu, H, out=out))
+    ms_exact = loop(lambda i: qfa.fp8_varlen_attn(q8, k8, v8, sc, cu, H, out=out))
+    del q8, k8, v8, exact, fast
+    exact = qfa.fp8_varlen_attn(*workload_codes, cu, H).float()
+    fast = qfa.fp8_varlen_attn_fp8qk(*workload_codes, cu, H).float()
+    e_out = ((fast - exact).abs() / exact.abs().clamp(min=1.0)).max().item()
+    tf = w.attn_flop / (ms_fast * 1e-3) / 1e12
+    return {"inputs": "the workload's shape and per-head sigmas, no outliers", "kernel": "attn_fwd_kernel<WaveF8<4, 8>, false>",
+            "ms": round(ms_fast, 4), "tflops": round(tf, 1), "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4),
+            "exact_kernel_ms": round(ms_exact, 4), "speedup_vs_exact": round(ms_exact / ms_fast, 3),
+            "max_e_vs_exact_kernel": float(f"{e:.3e}"),
+            "max_e_vs_exact_kernel_on_the_workloads_outliers": float(f"{e_out:.3e}")}
+
+
 def as_specified(w, qfa, torch, cu, out, stream):
     """The workload as its recipe states it: a fresh scale state and its own forwards' draws (16 distinct input
     sets, so the ring maximum moves and some forwards quantize a tensor twice).  Each forward's quantize and
@@ -660,6 +717,19 @@ def power_profile(seconds):
     ms, n, smp = sustained(lambda i: qfa.bf16_varlen_attn(*sets[i % len(sets)], cu, H, out=out), seconds, stream,
                            gpu)
     report("bf16_attention " + w.name, ms, n, smp, flop)
+
+    # Q K^T on the fp8 MFMA, on codes of the same shape and per-head sigmas without outliers (its domain), and the
+    # exact kernel on those same codes
+    import dataclasses
+
+    st_f = qfa.init_scale_state(dev)
+    f8 = qfa.quantize_qkv(st_f, "dynamic", *make_qkv(dataclasses.replace(w, outlier_p=0.0, outlier_scale=1.0), 0,
+                                                     device=dev))
+    sc_f = qfa.descale(st_f)
+    ms, n, smp = sustained(lambda i: qfa.fp8_varlen_attn_fp8qk(*f8, sc_f, cu, H, out=out), seconds, stream, gpu)
+    report("fp8qk_attention, no outliers " + w.name, ms, n, smp, flop)
+    ms, n, smp = sustained(lambda i: qfa.fp8_varlen_attn(*f8, sc_f, cu, H, out=out), seconds, stream, gpu)
+    report("fp8_attention, no outliers " + w.name, ms, n, smp, flop)
 
     for kind in BURN_KINDS:
         ms, n, smp, flop_burn, extra = mfma_burn_sustained(kind, seconds, stream, gpu)
@@ -909,14 +979,19 @@ def main():
                      "kernel": "attn_fwd_kernel", "flop_per_launch": flop},
         "design_mfma_ceiling": {
             "frac_fp8_peak": 0.5,
-            "why": "both products run on the fp16 MFMA (exact for E4M3 codes; half the fp8 rate) because gfx950's "
-                   "fp8 MFMAs truncate inside each group of 8 products (tests/test_gpu_mfma_hw.py), which on this "
-                   "workload's outliers breaks the accuracy bound (tests/test_fp8_mfma_emulation.py)",
+            "why": "the path runs both products on the fp16 MFMA (exact for E4M3 codes; half the fp8 rate) because "
+                   "gfx950's fp8 MFMAs truncate inside each group of 8 products (tests/test_gpu_mfma_hw.py), which on "
+                   "this workload's outliers breaks the accuracy bound (tests/test_fp8_mfma_emulation.py); "
+                   "fp8_varlen_attn_fp8qk runs Q K^T on the fp8 MFMA for Q and K without outliers "
+                   "(fp8_qk_outlier_free)",
             "frac_of_ceiling": round(attn_tflops / FP8_PEAK_TFLOPS / 0.5, 4)},
         "wall_s_timed_region": round(wall, 4),
     }
     if w.index == 3 and not args.no_as_specified:
         res["as_specified"] = as_specified(w, qfa, torch, cu, out, stream)
+    if not args.no_fp8qk:
+        res["fp8_qk_outlier_free"] = fp8qk_outlier_free(w, qfa, torch, cu, out, stream, args.steps,
+                                                        (q8, k8, v8, scales))
     if not args.no_power_limited:
         res["power_limited"] = power_limited(lambda i: qfa.fp8_varlen_attn(q8, k8, v8, scales, cu, H, out=out),
                                              flop, 2.0, stream)
