@@ -179,7 +179,7 @@ def _expected_requant(ost, observed):
     return [int(np.float32(observed[t]) > others[t]) for t in range(3)]
 
 
-@pytest.mark.parametrize("T,H", [(300, 2), (4096, 16)])
+@pytest.mark.parametrize("T,H", [(1, 1), (256, 2), (512, 1), (300, 2), (4096, 16)])
 def test_single_pass_and_second_pass(T, H):
     """Codes, ring and scales bit-exact on every forward, whichever pass produced them, and the
     requantized flag as the ring dictates."""
@@ -203,9 +203,10 @@ def test_single_pass_and_second_pass(T, H):
     assert seen == {0, 1}
 
 
-def test_single_pass_packed():
+@pytest.mark.parametrize("T,H", [(170, 3), (777, 3)])
+def test_single_pass_packed(T, H):
     """The same sequence through the fused [T, 3, H, D] entry point (D = 80)."""
-    T, H, D = 777, 3, 80
+    D = 80
     st = qfa.init_scale_state(DEV, history_len=4)
     ost = oracle.ScaleState(history_len=4)
     for fwd in range(len(_AMAX_SEQ[0])):
@@ -220,3 +221,26 @@ def test_single_pass_packed():
         assert np.array_equal(np.array(snap["descale"], np.float32), descale)
         for gg, oo in zip(g, (o8q, o8k, o8v)):
             assert np.array_equal(codes(gg), oo), fwd
+
+
+def test_paths_share_one_state():
+    """Forwards of varying size on one state (so a varying number of amax partials per tensor), switching
+    between the split and fused entry points: ring, cursor, scales, requantized flags and codes bit-exact
+    against the oracle after every forward."""
+    st = qfa.init_scale_state(DEV, history_len=4)
+    ost = oracle.ScaleState(history_len=4)
+    shapes = [(256, 2), (2048, 4), (100, 5), (300, 2), (64, 8), (1000, 1), (512, 1), (4096, 16), (3, 2), (700, 1)]
+    for fwd, (T, H) in enumerate(shapes):
+        xs = [_with_amax((T, H, 128), _AMAX_SEQ[t][fwd], seed=13 * fwd + t) for t in range(3)]
+        observed = [oracle.amax(bf16_to_f32(x)) for x in xs]
+        want_requant = _expected_requant(ost, observed)
+        if fwd % 3 == 2:
+            outs = qfa.quantize_qkv_packed(st, "dynamic", torch.stack(xs, dim=1).contiguous().to(DEV))
+        else:
+            outs = qfa.quantize_qkv(st, "dynamic", *[x.to(DEV) for x in xs])
+        _, inv = ost.forward_dynamic(observed)
+        snap = qfa.read_scale_state(st)
+        _state_equal(snap, ost)
+        assert snap["requantized"] == want_requant, (fwd, T, H, snap["requantized"], want_requant)
+        for t in range(3):
+            assert np.array_equal(codes(outs[t]), oracle.quantize(bf16_to_f32(xs[t]), inv[t])), (fwd, T, H, t)
