@@ -9,7 +9,8 @@ against the oracle:
   128, 96 and 80 (the fp8 kernels) and 64 (the exact kernel);
 - one-token sequences return their V row bit for bit;
 - the 2304-token image (static scales) on every row, and the QHD batch of
-  three 14400-token images (dynamic scales) on sampled rows of each image.
+  three 14400-token images (dynamic and static scales) on sampled rows of
+  each image.
 """
 
 import numpy as np
@@ -52,7 +53,7 @@ def test_fp8qk_ragged(seqlens, D):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("widx,mode", [(2, "static"), (4, "dynamic")])
+@pytest.mark.parametrize("widx,mode", [(2, "static"), (4, "dynamic"), (4, "static")])
 def test_fp8qk_outlier_free_workloads(widx, mode):
     w = WORKLOADS[widx]
     assert w.outlier_p == 0.0
