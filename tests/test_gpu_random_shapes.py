@@ -11,6 +11,8 @@ Each case draws, from numpy's PCG64 seeded with 1000 + case:
 
 The path is the fused-QKV quantize (dynamic, from [T, 3, H, D]) and both
 attention launches: unsplit, and split into the drawn number of ranges.
+Cases drawn without outliers also run the attention with Q K^T on the fp8
+MFMA (qfa_fp8_varlen_attn_fp8qk, whose domain they are), to the same bar.
 Codes and scales must match the oracle bit for bit; both outputs are held to
 the contract's tolerance and the kernel's own bound (tests/helpers.py)
 against the oracle's float64 attention over the D real dims.  Every case
@@ -71,3 +73,6 @@ def test_random_shape(case):
     assert_fp8_attn_close(bf16_to_f32(out), ref, f"case {case} unsplit", mag=mag)
     out_s = qfa.fp8_varlen_attn_split(q8, k8, v8, qfa.descale(st), cu, H, head_dim=D, num_splits=splits)
     assert_fp8_attn_close(bf16_to_f32(out_s), ref, f"case {case} split {splits}", mag=mag)
+    if outliers == 0.0:
+        out_f = qfa.fp8_varlen_attn_fp8qk(q8, k8, v8, qfa.descale(st), cu, H, head_dim=D)
+        assert_fp8_attn_close(bf16_to_f32(out_f), ref, f"case {case} fp8 Q K^T", mag=mag)
