@@ -20,6 +20,10 @@ contract's measure e = |g - r| / max(1, |r|):
   elements) breaks it on the rows that hold outliers: a product of two
   outliers truncates its 7 group-mates and moves the row's dominant logits.
 
+* on seeded Gaussian inputs the error grows with the logits' scale
+  (sigma^2) times the outliers' size: sigma 1 keeps x20 outliers (0.1 % of
+  the elements) inside the contract, sigma 3 does not keep x10 ones.
+
 So fp8 Q K^T is exact enough only for inputs known to be free of outliers,
 which the per-tensor scales cannot tell apart, and not for the workload the
 library is measured on: that is the domain of the fp8 entry point, and the
@@ -31,7 +35,7 @@ import pytest
 
 import oracle
 from test_gpu_mfma_hw import CASES, FP8_OBSERVED
-from workloads import WORKLOADS, make_qkv
+from workloads import WORKLOADS, make_qkv, random_qkv
 
 TOL_MAX = 3e-2
 
@@ -121,3 +125,36 @@ def test_outliers_break_the_contract():
     # largest codes are rows whose leading logits the truncation moves far
     # enough to shift the softmax weights
     assert _worst_error(3, "dynamic", (1, 4), 128) > TOL_MAX
+
+
+def _random_case_error(sigma, scale, T=2048, H=4, seed=23, rows_per_head=48):
+    """Max contract error of fp8-MFMA Q K^T on Gaussian Q, K, V of standard deviation sigma with 0.1 % of the
+    elements `scale` times larger (dynamic scales), over each head's rows with the largest |code|."""
+    q, k, v = random_qkv([T], H, seed=seed, sigma=sigma, outlier_p=0.001, outlier_scale=scale)
+    q8, k8, v8, (s_q, s_k, s_v), _ = oracle.quantize_qkv(oracle.ScaleState(), "dynamic",
+                                                         *(t.float().numpy() for t in (q, k, v)))
+    c = float(s_q) * float(s_k) / np.sqrt(128.0)
+    worst = 0.0
+    for h in range(H):
+        qd = oracle.decode(q8[:, h]).astype(np.float64)
+        kd = oracle.decode(k8[:, h]).astype(np.float64)
+        vd = oracle.decode(v8[:, h]).astype(np.float64) * float(s_v)
+        rows = np.argsort(-np.abs(qd).max(-1), kind="stable")[:rows_per_head]
+
+        def attend(s):
+            z = s * c
+            p = np.exp(z - z.max(-1, keepdims=True))
+            return (p / p.sum(-1, keepdims=True)) @ vd
+
+        r = attend(qd[rows] @ kd.T)
+        g = attend(_fp8_mfma_logits_chunked(qd[rows], kd))
+        worst = max(worst, float((np.abs(g - r) / np.maximum(1.0, np.abs(r))).max()))
+    return worst
+
+
+@pytest.mark.timeout(300)
+def test_domain_depends_on_logit_scale_and_outlier_size():
+    # the error grows with the logits' scale (sigma^2) times the outliers' size: unit-sigma inputs keep x20
+    # outliers inside the contract, sigma-3 inputs do not keep x10 ones
+    assert _random_case_error(1.0, 20.0) < TOL_MAX
+    assert _random_case_error(3.0, 10.0) > TOL_MAX
