@@ -80,6 +80,14 @@ def attn_errors(g, r, scale=None, unit=1.0):
     return float(e.max()), float(e.mean())
 
 
+def one_token_row(v_codes, s_v) -> torch.Tensor:
+    """The bf16 output of a one-token sequence, from its V codes (any shape) and s_v: fp32(v * s_v) rounded to
+    bf16, with a zero as +0.  The output is a sum of p * v terms that starts from +0 (in the kernels and in the
+    oracle alike), so a code of -0 comes out as +0."""
+    v = oracle.decode(np.asarray(v_codes)).astype(np.float32) * np.float32(s_v)
+    return torch.from_numpy(v + np.float32(0.0)).to(torch.bfloat16)
+
+
 def check_rows(w):
     """Query rows checked against the oracle at full size: every row, or the
     workload's stated row ranges in full."""

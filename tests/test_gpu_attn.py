@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import quantized_flash_attn_amd as qfa
-from helpers import (assert_fp8_attn_close, bf16_to_f32, check_rows, codes, log,
+from helpers import (assert_fp8_attn_close, bf16_to_f32, check_rows, codes, log, one_token_row,
                      oracle_attention_rows)
 from workloads import WORKLOADS, cu_seqlens_tensor, make_qkv, ramp_qkv, random_qkv
 
@@ -153,12 +153,32 @@ def test_one_token_sequence_returns_v_row():
     (q8, k8, v8), out, st = gpu_path(q, k, v, seqlens)
     s_v = np.float32(qfa.read_scale_state(st)["descale"][2])
     for row in (5, 15):
-        want = (oracle.decode(codes(v8)[row]).astype(np.float32) * s_v).astype(np.float32)
-        want_bf16 = torch.from_numpy(want).to(torch.bfloat16)
+        want_bf16 = one_token_row(codes(v8)[row], s_v)
         got = out[row].cpu()
         log(f"  row {row}: {int((got.view(torch.int16) == want_bf16.view(torch.int16)).sum())} of {got.numel()} "
             "bit-equal")
         assert torch.equal(got.view(torch.int16), want_bf16.view(torch.int16)), row
+
+
+def test_one_token_row_with_negative_zero_codes():
+    """V codes of -0 (tiny negative inputs) in a one-token sequence: the output is a sum of p * v terms that starts
+    from +0, as in the oracle, so those dims come out +0 and the rest bit for bit; both entry points."""
+    seqlens = [3, 1]
+    q, k, v = random_qkv(seqlens, 2, seed=21, device=DEV, sigma=2.0)
+    v[3, :, :8] = -1e-30   # far below the smallest E4M3 step at this scale: code 0x80
+    st = qfa.init_scale_state(DEV)
+    q8, k8, v8 = qfa.quantize_qkv(st, "dynamic", q, k, v)
+    assert (codes(v8)[3, :, :8] == 0x80).all()
+    s_v = qfa.read_scale_state(st)["descale"][2]
+    want = one_token_row(codes(v8)[3], s_v)
+    assert not torch.signbit(want[:, :8]).any()
+    cu = cu_seqlens_tensor(seqlens, DEV)
+    ref = oracle.attention(codes(q8), codes(k8), codes(v8), np.array(qfa.read_scale_state(st)["descale"], np.float32),
+                           np.concatenate([[0], np.cumsum(seqlens)]))
+    assert not np.signbit(ref[3, :, :8]).any()
+    for fn in (qfa.fp8_varlen_attn, qfa.fp8_varlen_attn_fp8qk):
+        out = fn(q8, k8, v8, qfa.descale(st), cu, 2)
+        assert torch.equal(out[3].cpu().view(torch.int16), want.view(torch.int16)), fn.__name__
 
 
 def test_identical_keys_give_mean_of_v():

@@ -8,6 +8,8 @@ against the oracle:
   span several tiles, empty sequences and one-token sequences, at head dims
   128, 96 and 80 (the fp8 kernels) and 64 (the exact kernel);
 - one-token sequences return their V row bit for bit;
+- the largest head count the ABI accepts (65536), sequences of 2 and 1
+  tokens, on sampled heads;
 - the 2304-token image (static scales) on every row, and the QHD batch of
   three 14400-token images (dynamic and static scales) on sampled rows of
   each image.
@@ -19,7 +21,7 @@ import torch
 
 import oracle
 import quantized_flash_attn_amd as qfa
-from helpers import assert_fp8_attn_close, bf16_to_f32, codes, log, oracle_attention_rows
+from helpers import assert_fp8_attn_close, bf16_to_f32, codes, log, one_token_row, oracle_attention_rows
 from workloads import WORKLOADS, cu_seqlens_tensor, make_qkv, random_qkv
 
 pytestmark = pytest.mark.gpu
@@ -47,9 +49,8 @@ def test_fp8qk_ragged(seqlens, D):
     for b, n in enumerate(seqlens):
         if n == 1:
             row = int(cu[b])
-            want = oracle.decode(codes(v8)[row, :, :D]).astype(np.float32) * np.float32(descale[2])
-            got = out[row].cpu().view(torch.int16)
-            assert torch.equal(got, torch.from_numpy(want).to(torch.bfloat16).view(torch.int16)), row
+            want = one_token_row(codes(v8)[row, :, :D], descale[2])
+            assert torch.equal(out[row].cpu().view(torch.int16), want.view(torch.int16)), row
 
 
 @pytest.mark.timeout(600)
@@ -78,3 +79,22 @@ def test_fp8qk_outlier_free_workloads(widx, mode):
     ref, mag = oracle_attention_rows(codes(q8), codes(k8), codes(v8), descale, cu, rows)
     got = bf16_to_f32(out[torch.from_numpy(rows).to(DEV)])
     assert_fp8_attn_close(got, ref, f"fp8qk workload {widx} {mode}", mag=mag)
+
+
+def test_fp8qk_max_heads():
+    seqlens, H = [2, 1], 65536
+    log(f"fp8qk seqlens={seqlens} H={H}")
+    q, k, v = random_qkv(seqlens, H, seed=47, device=DEV, sigma=1.5)
+    st = qfa.init_scale_state(DEV)
+    c8 = qfa.quantize_qkv(st, "dynamic", q, k, v)
+    out = qfa.fp8_varlen_attn_fp8qk(*c8, qfa.descale(st), cu_seqlens_tensor(seqlens, DEV), H)
+    descale = np.array(qfa.read_scale_state(st)["descale"], np.float32)
+    heads = np.unique(np.concatenate([np.arange(256), np.arange(H - 256, H),
+                                      np.random.default_rng(47).integers(0, H, size=512)]))
+    cu = np.concatenate([[0], np.cumsum(seqlens)])
+    ref, mag = oracle.attention(*(codes(t)[:, heads] for t in c8), descale, cu, magnitude=True)
+    assert_fp8_attn_close(bf16_to_f32(out)[:, heads], ref, f"fp8qk {H} heads", mag=mag)
+    # the one-token sequence returns its V row
+    want = one_token_row(codes(c8[2])[2, heads], descale[2])
+    got = out[2, torch.from_numpy(heads).to(DEV)].cpu().view(torch.int16)
+    assert torch.equal(got, want.view(torch.int16))

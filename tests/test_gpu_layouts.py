@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import quantized_flash_attn_amd as qfa
-from helpers import assert_fp8_attn_close, bf16_to_f32, codes, log
+from helpers import assert_fp8_attn_close, bf16_to_f32, codes, log, one_token_row
 from workloads import cu_seqlens_tensor, random_qkv
 
 pytestmark = pytest.mark.gpu
@@ -55,5 +55,5 @@ def test_layouts_agree_with_the_oracle(seqlens):
             continue
         row = int(cu[b])
         for out, v8, h in ((small, v8s, 0), (small, v8s, 1), (big, v8b, 0), (big, v8b, H_BIG - 1)):
-            want = torch.from_numpy(oracle.decode(codes(v8)[row, h]).astype(np.float32) * np.float32(ds[2]))
-            assert torch.equal(out[row, h].cpu().view(torch.int16), want.to(torch.bfloat16).view(torch.int16)), (row, h)
+            want = one_token_row(codes(v8)[row, h], ds[2])
+            assert torch.equal(out[row, h].cpu().view(torch.int16), want.view(torch.int16)), (row, h)

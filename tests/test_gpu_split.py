@@ -15,7 +15,8 @@ import torch
 
 import oracle
 import quantized_flash_attn_amd as qfa
-from helpers import assert_fp8_attn_close, bf16_to_f32, check_rows, codes, log, oracle_attention_rows
+from helpers import (assert_fp8_attn_close, bf16_to_f32, check_rows, codes, log, one_token_row,
+                     oracle_attention_rows)
 from workloads import WORKLOADS, cu_seqlens_tensor, make_qkv, random_qkv
 
 pytestmark = pytest.mark.gpu
@@ -77,8 +78,8 @@ def test_split_one_token_rows_and_determinism():
     assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
     s_v = np.float32(qfa.read_scale_state(st)["descale"][2])
     for row in (5, 306):
-        want = torch.from_numpy((oracle.decode(codes(v8)[row]).astype(np.float32) * s_v).astype(np.float32))
-        assert torch.equal(out1[row].cpu().view(torch.int16), want.to(torch.bfloat16).view(torch.int16)), row
+        want = one_token_row(codes(v8)[row], s_v)
+        assert torch.equal(out1[row].cpu().view(torch.int16), want.view(torch.int16)), row
 
 
 def test_split_no_leakage():
